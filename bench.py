@@ -1,0 +1,161 @@
+"""Benchmark of the DualQuant BCD solver on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic weight matrix:
+dq_init_rtn (absmax RTN), dq_bcd_iterate(T) and dq_pack_codes, with W
+already resident in HBM. The workload is a 4096x4096 bf16 q_proj-shaped
+matrix, N(0, 0.02^2) with 1 % outlier columns scaled by U[10, 50], INT4
+codes, G = 64, fp16 block and column scales, T = 20 iterations.
+
+value = rows * cols * T * steps / (time of the timed steps): weight elements
+per second per BCD iteration, whole job (init and pack included). The
+roofline entry is for the dominant kernel, the BCD pass: its algorithmic
+bytes per launch (one read of W plus a read and a write of the block scales
+and the column scales) over its average duration, measured with events on
+the stream the kernel runs on. cpu_baseline times the float64 oracle on
+the host (test infrastructure, never on the product path).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def alg_bytes_per_elem(w_bytes: int, a_bytes: int, G: int, rows: int) -> float:
+    """One read of W, a read and a write of the block scales, a read and a
+    write of the column scales (2 bytes each, amortized over the rows)."""
+    return w_bytes + 2.0 * a_bytes / G + 4.0 / rows
+
+
+def cpu_baseline(wl, data, budget_s: float = 30.0):
+    """Time the float64 oracle on the same workload (whole matrix when it
+    fits the budget, else a prefix of whole column stripes)."""
+    from oracle import dualquant as D
+    from calibration_free_bit_amd import synth
+
+    W = synth.bf16_to_f64(data) if data.dtype.name == "uint16" else data.astype("float64")
+    fmt = D.FORMATS[wl.fmt]
+    # calibrate on 2 stripes, then size the sample
+    G = fmt.group
+    t0 = time.perf_counter()
+    D.solve(W[:, :2 * G], fmt, wl.iters)
+    rate = 2 * G * W.shape[0] * wl.iters / (time.perf_counter() - t0)
+    n_str = W.shape[1] // G
+    k = max(2, min(n_str, int(budget_s * 0.6 * rate / (G * W.shape[0] * wl.iters))))
+    Ws = W[:, :k * G]
+    t0 = time.perf_counter()
+    D.solve(Ws, fmt, wl.iters)
+    dt = time.perf_counter() - t0
+    sample = (f"float64 numpy oracle, {'whole matrix' if k == n_str else f'first {k} of {n_str} column stripes'}"
+              f" ({Ws.shape[0]}x{Ws.shape[1]}), T={wl.iters}, {dt:.1f} s")
+    return {"value": Ws.size * wl.iters / dt, "unit": "elements/s", "cores": 1,
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; "
+              "the solver shards by column stripes with no communication, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from calibration_free_bit_amd import dq, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    fmt = dq.FORMATS[wl.fmt]
+    m = synth.make_matrix(wl.spec, wl.seeds[0])
+    data = m.data
+    host = torch.from_numpy(data.view(np.int16) if data.dtype == np.uint16 else data)
+    W = host.to("cuda:0")
+    s = dq.Solver(W, fmt)
+    M, N = W.shape
+    T = wl.iters
+    st = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        s.solve(T)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(st)
+        s.init()
+        e[1].record(st)
+        s.iterate(T)
+        e[2].record(st)
+        s.pack()
+        e[3].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    init_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    iter_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    pack_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    elems = M * N
+    value = elems * T / (step_ms * 1e-3)
+    pass_s = iter_ms * 1e-3 / T
+    w_bytes = 2 if fmt_w_bf16(data) else 4
+    a_bytes = 2 if fmt.a_fmt == dq.SCALE_FP16 else 1
+    b_alg = alg_bytes_per_elem(w_bytes, a_bytes, fmt.group, M)
+    achieved = b_alg * elems / pass_s / 1e9
+
+    out = {
+        "metric": "weight elements/s per BCD iteration",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32-requant/f64-sums",
+        "data": "synthetic (seeded, numpy PCG64)",
+        "config": {"workload": wl.name, "rows": M, "cols": N, "format": wl.fmt,
+                   "group": fmt.group, "iters": T, "seed": wl.seeds[0],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "bcd_pass_kernel", "alg_bytes_per_elem": b_alg,
+                     "avg_launch_us": pass_s * 1e6},
+        "breakdown_ms": {"init": init_ms, "iterate": iter_ms, "pack": pack_ms,
+                         "wall_per_step": wall * 1e3 / args.steps},
+        "iterate_elements_per_s_per_iter": elems / pass_s,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, data)
+    print(json.dumps(out))
+
+
+def fmt_w_bf16(data) -> bool:
+    return data.dtype.name == "uint16"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+// dq_api.hip -- the C ABI declared in include/dq.h: argument validation,
+// workspace sizing and dispatch to the templated kernels. Everything is
+// enqueued on the caller's stream; nothing is allocated.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "dq.h"
+#include "dq_device.h"
+#include "dq_kernels.h"
+
+namespace {
+
+using dq::PassGeom;
+
+constexpr int kAbiVersion = 1;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int elem_size(int32_t w_type) { return w_type == DQ_W_F32 ? 4 : 2; }
+
+// Shape and format checks shared by every entry point.
+int check_problem(const dq_problem* p) {
+  if (!p) return DQ_ERR_INVALID_ARG;
+  if (p->group != 16 && p->group != 32 && p->group != 64) return DQ_ERR_UNSUPPORTED;
+  if (p->grid != DQ_GRID_INT4 && p->grid != DQ_GRID_E2M1) return DQ_ERR_UNSUPPORTED;
+  if (p->a_fmt != DQ_SCALE_FP16 && p->a_fmt != DQ_SCALE_E8M0 && p->a_fmt != DQ_SCALE_E4M3)
+    return DQ_ERR_UNSUPPORTED;
+  if (p->b_fmt != DQ_SCALE_FP16) return DQ_ERR_UNSUPPORTED;
+  if (p->w_type != DQ_W_F32 && p->w_type != DQ_W_BF16) return DQ_ERR_UNSUPPORTED;
+  if (p->rows < 1 || p->cols < 1 || p->cols % p->group != 0) return DQ_ERR_SHAPE;
+  if (p->ldw < p->cols || (p->ldw * elem_size(p->w_type)) % 16 != 0) return DQ_ERR_SHAPE;
+  if (p->rows > (int64_t(1) << 40) / p->ldw) return DQ_ERR_SHAPE;  // keep offsets far from overflow
+  return DQ_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+struct Workspace {
+  PassGeom g;
+  size_t counter_off, bytes;
+};
+
+Workspace pass_geometry(const dq_problem* p) {
+  Workspace w{};
+  PassGeom& g = w.g;
+  g.ldw = p->ldw;
+  g.M = p->rows;
+  g.N = p->cols;
+  g.S = ceil_div(p->rows, dq::kRowsPerStep);
+  g.n_tiles = ceil_div(p->cols, dq::kTileCols);
+  g.total = g.S * g.n_tiles;
+  g.L = ceil_div(g.total, dq::kPassGrid);
+  g.n_wg = ceil_div(g.total, g.L);
+  g.max_seg = 0;
+  for (int64_t t = 0; t < g.n_tiles; ++t) {
+    const int64_t first = (t * g.S) / g.L, last = ((t + 1) * g.S - 1) / g.L;
+    g.max_seg = std::max(g.max_seg, last - first + 1);
+  }
+  const size_t part_bytes = size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double);
+  w.counter_off = align256(part_bytes);
+  w.bytes = w.counter_off + align256(size_t(g.n_tiles) * sizeof(uint32_t));
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DQ_OK : DQ_ERR_HIP; }
+
+// Calls f.template operator()<WT, GRID, AFMT, G>() for p's format.
+template <class F>
+int dispatch(const dq_problem& p, F&& f) {
+  auto by_group = [&]<int WT, int GR, int AF>() -> int {
+    switch (p.group) {
+      case 16: return f.template operator()<WT, GR, AF, 16>();
+      case 32: return f.template operator()<WT, GR, AF, 32>();
+      case 64: return f.template operator()<WT, GR, AF, 64>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  auto by_afmt = [&]<int WT, int GR>() -> int {
+    switch (p.a_fmt) {
+      case DQ_SCALE_FP16: return by_group.template operator()<WT, GR, dq::kScaleFp16>();
+      case DQ_SCALE_E8M0: return by_group.template operator()<WT, GR, dq::kScaleE8M0>();
+      case DQ_SCALE_E4M3: return by_group.template operator()<WT, GR, dq::kScaleE4M3>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  auto by_grid = [&]<int WT>() -> int {
+    switch (p.grid) {
+      case DQ_GRID_INT4: return by_afmt.template operator()<WT, dq::kGridInt4>();
+      case DQ_GRID_E2M1: return by_afmt.template operator()<WT, dq::kGridE2M1>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  switch (p.w_type) {
+    case DQ_W_F32: return by_grid.template operator()<dq::kWF32>();
+    case DQ_W_BF16: return by_grid.template operator()<dq::kWBF16>();
+  }
+  return DQ_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dq_abi_version(void) { return kAbiVersion; }
+
+const char* dq_status_string(int status) {
+  switch (status) {
+    case DQ_OK: return "ok";
+    case DQ_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad count)";
+    case DQ_ERR_SHAPE: return "inconsistent shape (rows/cols/ld, or cols not a multiple of G)";
+    case DQ_ERR_UNSUPPORTED: return "unsupported format combination";
+    case DQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case DQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t dq_workspace_bytes(const dq_problem* p) {
+  if (check_problem(p) != DQ_OK) return 0;
+  return pass_geometry(p).bytes;
+}
+
+int dq_init_rtn(const dq_problem* p, const void* W, void* a, uint16_t* b, void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (!W || !a || !b || !aligned16(W)) return DQ_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_init<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, st));
+  });
+}
+
+int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int32_t n_iters,
+                   void* workspace, size_t workspace_bytes, double* stats, void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (!W || !a || !b || !aligned16(W) || n_iters < 0) return DQ_ERR_INVALID_ARG;
+  if (stats) return DQ_ERR_UNSUPPORTED;
+  if (n_iters == 0) return DQ_OK;
+  const Workspace ws = pass_geometry(p);
+  if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DQ_ERR_WORKSPACE;
+  double* part = static_cast<double*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws.counter_off);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, counters, ws.g, n_iters, st));
+  });
+}
+
+int dq_pack_codes(const dq_problem* p, const void* W, const void* a, const uint16_t* b,
+                  uint8_t* packed, void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (!W || !a || !b || !packed || !aligned16(W) || (reinterpret_cast<uintptr_t>(packed) & 7u))
+    return DQ_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_pack<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, packed, st));
+  });
+}
+
+int dq_rescale_quantize_act(const dq_problem* p, const void* X, int64_t tokens, int64_t ldx,
+                            const uint16_t* b, uint8_t* xq, void* x_scales, void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (p->w_type != DQ_W_BF16) return DQ_ERR_UNSUPPORTED;  // X' = X D_b is exact only for bf16 X
+  if (tokens < 0 || ldx < p->cols || (ldx * 2) % 16 != 0) return DQ_ERR_SHAPE;
+  if (tokens == 0) return DQ_OK;
+  if (!X || !b || !xq || !x_scales || !aligned16(X) || !aligned16(xq)) return DQ_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* Xh = static_cast<const uint16_t*>(X);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    if constexpr (WT != dq::kWBF16) {
+      return int(DQ_ERR_UNSUPPORTED);
+    } else {
+      return hip_status(dq::launch_act<GR, AF, G>(Xh, ldx, tokens, p->cols, b, xq, x_scales, st));
+    }
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+// dq_device.h -- device-side number formats for the DualQuant kernels (gfx950).
+//
+// Element grids ("DualQuant" paper summary §3: integer formats round and
+// clip, floating-point formats take the nearest level of their grid):
+//   INT4  integers [-8, 7], round half to even, clip;
+//   E2M1  magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest, ties to the even
+//         encoding, saturating at 6.
+// Scale sets (summary §3; reproduction README "Core equations": inverse
+// scales are projected onto hardware-legal values):
+//   fp16  IEEE binary16, positive finite;
+//   E8M0  2^e, e in [-127, 127];
+//   E4M3  OCP E4M3FN without sign: k 2^-9 (k = 1..7) and 2^e (1 + m/8)
+//         up to 448.
+// Projection takes a positive float64 to the nearest legal value (ties to
+// even for fp16 / E4M3, upward for E8M0), clamped to the smallest legal
+// value and saturated at the largest.
+//
+// Requantization x = W / (a b) must be decided on the exact quotient. The
+// fast path evaluates y ~= x in float32 from precomputed reciprocals; its
+// relative error is at most 7 units of 2^-24, so for |x| <= 8.25 the error
+// is below 3.5e-6. Any element whose y lies within 2^-17 of a rounding
+// midpoint is flagged, and the caller then re-decides the whole group with
+// the exact path: the sign of W - m a b for the candidate midpoint m comes
+// from one fused multiply-add, exact because m*a is exact in float32 and
+// the FMA rounds W - (m a) b once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace dq {
+
+enum : int { kGridInt4 = 0, kGridE2M1 = 1 };
+enum : int { kScaleFp16 = 0, kScaleE8M0 = 1, kScaleE4M3 = 2 };
+enum : int { kWF32 = 0, kWBF16 = 1 };
+
+// |y - rint(y)| above this flags a possible misrounding (0.5 - 2^-17).
+constexpr float kTieFlag = 0.5f - 0x1p-17f;
+
+// ------------------------------------------------------------ scale codes
+
+// binade exponent k with 2^k <= x < 2^(k+1), for normal x > 0
+__device__ __forceinline__ int binade(double x) { return __builtin_amdgcn_frexp_exp(x) - 1; }
+
+template <int AFMT> struct ScaleStore;
+template <> struct ScaleStore<kScaleFp16> { using T = uint16_t; };
+template <> struct ScaleStore<kScaleE8M0> { using T = uint8_t; };
+template <> struct ScaleStore<kScaleE4M3> { using T = uint8_t; };
+
+__device__ __forceinline__ float fp16_bits_to_float(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+template <int AFMT>
+__device__ __forceinline__ float decode_scale(typename ScaleStore<AFMT>::T c) {
+  if constexpr (AFMT == kScaleFp16) {
+    return fp16_bits_to_float(c);
+  } else if constexpr (AFMT == kScaleE8M0) {
+    return __builtin_ldexpf(1.0f, (int)c - 127);
+  } else {
+    const int e = c >> 3, m = c & 7;
+    return e == 0 ? (float)m * 0x1p-9f : __builtin_ldexpf(1.0f + 0.125f * (float)m, e - 7);
+  }
+}
+
+// Code of a legal value (the value must already be legal).
+template <int AFMT>
+__device__ __forceinline__ typename ScaleStore<AFMT>::T encode_scale(double v) {
+  if constexpr (AFMT == kScaleFp16) {
+    return __half_as_ushort(__float2half_rn((float)v));
+  } else if constexpr (AFMT == kScaleE8M0) {
+    return (uint8_t)(binade(v) + 127);
+  } else {
+    if (v < 0x1p-6) return (uint8_t)(v * 512.0);
+    const int e = binade(v);
+    const int m = (int)((__builtin_ldexp(v, -e) - 1.0) * 8.0);
+    return (uint8_t)(((e + 7) << 3) | m);
+  }
+}
+
+// ------------------------------------------------------------- projection
+
+// Round x > 0 to a multiple of 2^lsb_exp, to nearest even, by adding and
+// removing 1.5 * 2^(lsb_exp + 52): the sum's unit in the last place is
+// exactly 2^lsb_exp. Needs x < 2^(lsb_exp + 52).
+__device__ __forceinline__ double round_to_exp(double x, int lsb_exp) {
+  const double c = __builtin_ldexp(1.5, lsb_exp + 52);
+  return (x + c) - c;
+}
+
+
+template <int AFMT>
+__device__ __forceinline__ double project(double x) {
+  if constexpr (AFMT == kScaleFp16) {
+    x = __builtin_fmin(__builtin_fmax(x, 0x1p-24), 65504.0);
+    const int k = max(binade(x), -14);            // below 2^-14: fixed 2^-24 step
+    return round_to_exp(x, k - 10);
+  } else if constexpr (AFMT == kScaleE4M3) {
+    x = __builtin_fmin(__builtin_fmax(x, 0x1p-9), 448.0);
+    const int k = max(binade(x), -6);             // below 2^-6: fixed 2^-9 step
+    return round_to_exp(x, k - 3);
+  } else {
+    x = __builtin_fmax(x, 0x1p-127);
+    int k = binade(x);                            // 2^k <= x < 2^(k+1)
+    if (x >= __builtin_ldexp(1.5, k)) k += 1;     // nearest; the midpoint goes up
+    return __builtin_ldexp(1.0, min(k, 127));
+  }
+}
+
+// Closed-form least-squares scale with the scale-1 rule for an all-zero
+// code slice (den == 0).
+template <int AFMT>
+__device__ __forceinline__ double ls_scale(double num, double den) {
+  return den > 0.0 ? project<AFMT>(num / den) : 1.0;
+}
+
+// ------------------------------------------------------- element quantizer
+
+template <int GRID> struct Grid;
+
+template <> struct Grid<kGridInt4> {
+  static constexpr float qmax = 7.0f;
+  // Fast path: y ~= x. Returns the code; accumulates |y - code| (in units
+  // of the grid step) into flag.
+  __device__ static __forceinline__ float fast(float y, float& flag) {
+    const float yc = __builtin_amdgcn_fmed3f(y, -8.25f, 7.25f);
+    const float q = __builtin_rintf(yc);
+    flag = __builtin_fmaxf(flag, __builtin_fabsf(yc - q));
+    return q;
+  }
+  // Exact path: y ~= x within 0.5, w = W, ab = a and b with m*a exact.
+  __device__ static __forceinline__ float exact(float y, float w, float a, float b) {
+    const float yc = __builtin_amdgcn_fmed3f(y, -8.25f, 7.25f);
+    const float k = __builtin_floorf(yc);
+    const float m = k + 0.5f;
+    const float d = __builtin_fmaf(-(m * a), b, w);   // sign of W - m a b, exact
+    const bool k_odd = ((int)k & 1) != 0;
+    const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
+    return __builtin_amdgcn_fmed3f(k + up, -8.0f, 7.0f);
+  }
+  __device__ static __forceinline__ uint32_t nibble(float q) {
+    return (uint32_t)((int)q) & 0xFu;
+  }
+};
+
+template <> struct Grid<kGridE2M1> {
+  static constexpr float qmax = 6.0f;
+  // In binade scale t = |y| * 2^s (s = 1 below 2, 0 below 4, -1 above) the
+  // E2M1 levels are consecutive integers and ties-to-even-encoding is
+  // ties-to-even on t. frexp_exp gives e with |y| in [2^(e-1), 2^e).
+  __device__ static __forceinline__ float fast(float y, float& flag) {
+    const float ay = __builtin_fminf(__builtin_fabsf(y), 6.25f);
+    const int s = max(-1, min(1, 2 - __builtin_amdgcn_frexp_expf(ay)));
+    const float t = __builtin_ldexpf(ay, s);
+    const float r = __builtin_rintf(t);
+    flag = __builtin_fmaxf(flag, __builtin_fabsf(t - r));
+    return __builtin_copysignf(__builtin_ldexpf(r, -s), y);
+  }
+  __device__ static __forceinline__ float exact(float y, float w, float a, float b) {
+    const float ay = __builtin_fminf(__builtin_fabsf(y), 6.25f);
+    const int s = max(-1, min(1, 2 - __builtin_amdgcn_frexp_expf(ay)));
+    const float t = __builtin_ldexpf(ay, s);
+    const float k = __builtin_floorf(t);
+    const float m = __builtin_ldexpf(k + 0.5f, -s);   // midpoint in |x| units
+    const float d = __builtin_fmaf(-(m * a), b, __builtin_fabsf(w));
+    const bool k_odd = ((int)k & 1) != 0;
+    const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
+    const float mag = __builtin_fminf(__builtin_ldexpf(k + up, -s), 6.0f);
+    return __builtin_copysignf(mag, w);
+  }
+  __device__ static __forceinline__ uint32_t nibble(float q) {
+    const float aq = __builtin_fabsf(q);
+    // level index: 0,.5,1,1.5 -> 0..3 ; 2,3 -> 4,5 ; 4 -> 6 ; 6 -> 7
+    const uint32_t idx = aq < 2.0f ? (uint32_t)(aq * 2.0f)
+                       : aq < 4.0f ? (uint32_t)aq + 2u
+                       : (aq < 5.0f ? 6u : 7u);
+    return idx | ((q < 0.0f) ? 8u : 0u);
+  }
+};
+
+// ---------------------------------------------------------------- W loads
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Load 8 consecutive elements starting at p (16-byte aligned for bf16,
+// 32 bytes = two 16-byte loads for float32) into float registers.
+template <int WT>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float* out) {
+  if constexpr (WT == kWBF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    const float4 v0 = p[0], v1 = p[1];
+    out[0] = v0.x; out[1] = v0.y; out[2] = v0.z; out[3] = v0.w;
+    out[4] = v1.x; out[5] = v1.y; out[6] = v1.z; out[7] = v1.w;
+  }
+}
+
+}  // namespace dq

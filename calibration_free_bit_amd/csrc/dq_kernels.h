@@ -1,0 +1,47 @@
+// dq_kernels.h -- launch interface between the C ABI (dq_api.hip) and the
+// kernels (dq_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dq {
+
+constexpr int kTileCols = 64;   // columns of one independent tile
+constexpr int kLaneCols = 16;   // contiguous columns one lane owns
+constexpr int kRowsPerStep = 4 * 64 * kLaneCols / kTileCols;  // rows per workgroup step
+constexpr int kPassGrid = 512;  // target workgroups of one BCD pass
+
+// Geometry of one BCD pass. Work is the flattened list of (tile, row step)
+// pairs, tile-major; workgroup w owns steps [w L, (w+1) L). The workgroups
+// that touch tile t are floor(t S / L) .. floor(((t+1) S - 1) / L); each
+// writes one partial (segment) per column of t.
+struct PassGeom {
+  int64_t ldw, M, N;
+  int64_t S;        // row steps per tile
+  int64_t n_tiles;  // column tiles
+  int64_t total;    // n_tiles * S
+  int64_t L;        // row steps per workgroup
+  int64_t n_wg;     // workgroups launched
+  int64_t max_seg;  // most segments any tile has
+};
+// Workspace: part [n_tiles][max_seg][64][2] float64 column partial sums,
+// then counters [n_tiles] uint32 (zero between passes).
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
+                       hipStream_t st);
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, uint32_t* counters,
+                          const PassGeom& g, int n_iters, hipStream_t st);
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
+                       const uint16_t* b, uint8_t* packed, hipStream_t st);
+
+template <int GRID, int AFMT, int G>
+hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, const uint16_t* b,
+                      uint8_t* xq, void* xs, hipStream_t st);
+
+}  // namespace dq

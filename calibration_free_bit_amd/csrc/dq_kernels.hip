@@ -1,0 +1,419 @@
+// dq_kernels.hip -- HIP kernels of the DualQuant solver for gfx950 (MI355X).
+//
+// One BCD iteration ("DualQuant" reproduction README, "Core equations" and
+// its flowchart; paper summary §4.3, App. A-B) is ONE pass over W:
+//
+//   for every (row i, block g):  Q1 = q(W/(a b))          (codes of the state)
+//                                a' = Pi(sum W R / sum R^2), R = Q1 D_b
+//                                Q2 = q(W/(a' b))          (requantize)
+//   for every column j:          b' = Pi(sum W S / sum S^2), S = D_a' Q2
+//
+// The row/block update only needs the G columns of its block and the column
+// update only needs a' of the same column stripe, so the problem splits into
+// independent 64-column tiles spanning all rows. A workgroup streams a range
+// of row steps of a tile: every lane owns kLaneCols contiguous columns of one
+// row, keeps those elements in registers between the two requantizations,
+// and accumulates float64 column sums for its columns across the rows it
+// visits. At the end of its range the workgroup
+// reduces those sums through LDS, writes one partial per column, and the
+// last workgroup to finish a tile (atomic counter) adds the partials in a
+// fixed order and writes b'. Q is never stored: it is recomputed from
+// (W, a, b) whenever needed, so one iteration reads W once.
+//
+// Every sum of the least-squares updates is accumulated in float64 in a
+// fixed order: each product is exact and, for bf16 weights, every partial
+// sum is exact, so the result does not depend on the order at all.
+#include <hip/hip_runtime.h>
+
+#include "dq_device.h"
+#include "dq_kernels.h"
+
+namespace dq {
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// ------------------------------------------------------------ small fills
+
+static __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------------ init
+
+// One thread per (row, block): absmax -> a = Pi(absmax / qmax), 1 if zero.
+template <int WT, int GRID, int AFMT, int G>
+__global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ W, int64_t ldw,
+                                                       int64_t M, int64_t N, void* __restrict__ a_,
+                                                       uint16_t* __restrict__ b) {
+  using AT = typename ScaleStore<AFMT>::T;
+  const int64_t nblk = N / G;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < M * nblk) {
+    const int64_t row = idx / nblk, blk = idx - row * nblk;
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < G / 8; ++c) {
+      float v[8];
+      load8<WT>(W, row * ldw + blk * G + 8 * c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[k]));
+    }
+    const double s = amax > 0.0f ? project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0;
+    reinterpret_cast<AT*>(a_)[idx] = encode_scale<AFMT>(s);
+  }
+  if (idx < N) b[idx] = 0x3C00u;  // fp16 1.0
+}
+
+// ------------------------------------------------------------ BCD pass
+
+constexpr int kThreads = 256;  // 4 waves
+
+template <int WT, int GRID, int AFMT, int G>
+__global__ void __launch_bounds__(kThreads, 2)
+    bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, uint16_t* __restrict__ b,
+                    double* __restrict__ part, uint32_t* __restrict__ counters, PassGeom g) {
+  using AT = typename ScaleStore<AFMT>::T;
+  constexpr int LC = kLaneCols;             // contiguous columns per lane
+  constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
+  constexpr int RPW = 64 / LPR;             // rows per wave per step
+  constexpr int RPS = 4 * RPW;              // rows per workgroup per step
+  constexpr int BL = G < LC ? G : LC;       // elements of one block inside a lane
+  constexpr int NB = LC / BL;               // blocks (or block parts) per lane
+  constexpr int LPB = G > LC ? G / LC : 1;  // lanes sharing one block
+  constexpr int kRedStride = RPS + 1;       // LDS pitch (doubles) of the reduction
+  static_assert(RPS == kRowsPerStep, "geometry mismatch");
+
+  __shared__ float s_b[kTileCols];
+  __shared__ float s_rb[kTileCols];
+  __shared__ double s_red[kTileCols * kRedStride];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPR, rl = lane / LPR;
+  const int64_t nblk = g.N / G;
+  AT* __restrict__ a = reinterpret_cast<AT*>(a_);
+
+  int64_t f = (int64_t)blockIdx.x * g.L;
+  const int64_t f_end = min(f + g.L, g.total);
+  while (f < f_end) {
+    const int64_t tile = f / g.S;
+    const int64_t seg_end = min(f_end, (tile + 1) * g.S);
+    const int64_t tcol = tile * kTileCols;
+
+    __syncthreads();  // LDS of the previous segment is no longer read
+    if (tid < kTileCols) {
+      const int64_t j = tcol + tid;
+      const float bj = j < g.N ? fp16_bits_to_float(b[j]) : 1.0f;
+      s_b[tid] = bj;
+      s_rb[tid] = 1.0f / bj;
+    }
+    __syncthreads();
+
+    const int64_t col0 = tcol + sub * LC;
+    const float* lb = s_b + sub * LC;
+    const float* lrb = s_rb + sub * LC;
+    double cn[LC], cd[LC];
+#pragma unroll
+    for (int e = 0; e < LC; ++e) { cn[e] = 0.0; cd[e] = 0.0; }
+
+    for (; f < seg_end; ++f) {
+      const int64_t row = (f - tile * g.S) * RPS + wave * RPW + rl;
+      const bool row_ok = row < g.M;
+
+      float w[LC];
+#pragma unroll
+      for (int c = 0; c < LC / 8; ++c) {
+        if (row_ok && col0 + 8 * c < g.N) {
+          load8<WT>(W, row * g.ldw + col0 + 8 * c, &w[8 * c]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) w[8 * c + k] = 0.0f;
+        }
+      }
+
+      float a_old[NB];
+      bool blk_ok[NB];
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        const int64_t c = col0 + bl * BL;
+        blk_ok[bl] = row_ok && c < g.N;
+        a_old[bl] = blk_ok[bl] ? decode_scale<AFMT>(a[row * nblk + c / G]) : 1.0f;
+      }
+
+      // Q1 = q(W / (a b)) with the current state, fused with the row/block
+      // least-squares sums (R = Q1 D_b). If any element of the wave lies
+      // near a rounding midpoint the sums are redone with exact codes.
+      double num[NB], den[NB];
+      float flag = 0.0f;
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        const float ra = __builtin_amdgcn_rcpf(a_old[bl]);
+        num[bl] = 0.0;
+        den[bl] = 0.0;
+#pragma unroll
+        for (int k = 0; k < BL; ++k) {
+          const int e = bl * BL + k;
+          const float q = Grid<GRID>::fast(w[e] * lrb[e] * ra, flag);
+          const double R = (double)(q * lb[e]);  // exact product
+          num[bl] = __builtin_fma((double)w[e], R, num[bl]);
+          den[bl] = __builtin_fma(R, R, den[bl]);
+        }
+      }
+      if (wave_any(flag > kTieFlag)) {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) {
+          const float ra = __builtin_amdgcn_rcpf(a_old[bl]);
+          num[bl] = 0.0;
+          den[bl] = 0.0;
+#pragma unroll
+          for (int k = 0; k < BL; ++k) {
+            const int e = bl * BL + k;
+            const float q = Grid<GRID>::exact(w[e] * lrb[e] * ra, w[e], a_old[bl], lb[e]);
+            const double R = (double)(q * lb[e]);
+            num[bl] = __builtin_fma((double)w[e], R, num[bl]);
+            den[bl] = __builtin_fma(R, R, den[bl]);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < LPB; m <<= 1) {  // blocks wider than a lane
+        num[0] += __shfl_xor(num[0], m);
+        den[0] += __shfl_xor(den[0], m);
+      }
+
+      // project, synchronize the copy that assigns codes, store
+      float a_new[NB];
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        const double an = ls_scale<AFMT>(num[bl], den[bl]);
+        a_new[bl] = (float)an;
+        if (blk_ok[bl] && (sub % LPB) == 0) a[row * nblk + (col0 + bl * BL) / G] = encode_scale<AFMT>(an);
+      }
+
+      // Q2 = q(W / (a' b))
+      float q[LC];
+      flag = 0.0f;
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
+#pragma unroll
+        for (int k = 0; k < BL; ++k) {
+          const int e = bl * BL + k;
+          q[e] = Grid<GRID>::fast(w[e] * lrb[e] * ra, flag);
+        }
+      }
+      if (wave_any(flag > kTieFlag)) {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) {
+          const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
+#pragma unroll
+          for (int k = 0; k < BL; ++k) {
+            const int e = bl * BL + k;
+            q[e] = Grid<GRID>::exact(w[e] * lrb[e] * ra, w[e], a_new[bl], lb[e]);
+          }
+        }
+      }
+
+      // column least-squares sums, S = D_a' Q2
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+#pragma unroll
+        for (int k = 0; k < BL; ++k) {
+          const int e = bl * BL + k;
+          const double S = (double)(a_new[bl] * q[e]);  // exact product
+          cn[e] = __builtin_fma((double)w[e], S, cn[e]);
+          cd[e] = __builtin_fma(S, S, cd[e]);
+        }
+      }
+    }
+
+    // ---- reduce the RPS row-lanes of each column, write this segment's partial
+    const int64_t first_wg = (tile * g.S) / g.L;
+    const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
+    const int64_t seg = (int64_t)blockIdx.x - first_wg;
+    double* __restrict__ pw = part + (tile * g.max_seg + seg) * (kTileCols * 2);
+#pragma unroll
+    for (int qn = 0; qn < 2; ++qn) {
+#pragma unroll
+      for (int e = 0; e < LC; ++e)
+        s_red[(sub * LC + e) * kRedStride + wave * RPW + rl] = qn ? cd[e] : cn[e];
+      __syncthreads();
+      const int c = tid >> 2, pi = tid & 3;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int r = 0; r < RPS / 4; ++r) acc += s_red[c * kRedStride + pi * (RPS / 4) + r];
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (pi == 0) pw[c * 2 + qn] = acc;
+      __syncthreads();
+    }
+
+    // ---- last workgroup of the tile: b' = Pi_fp16(sum num / sum den)
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old = atomicAdd(&counters[tile], 1u);
+      s_last = (int64_t)old == n_seg - 1;
+    }
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      if (tid < kTileCols) {
+        const double* pt = part + tile * g.max_seg * (kTileCols * 2) + tid * 2;
+        double nsum = 0.0, dsum = 0.0;
+        for (int64_t s = 0; s < n_seg; ++s) {
+          nsum += pt[s * (kTileCols * 2)];
+          dsum += pt[s * (kTileCols * 2) + 1];
+        }
+        const int64_t j = tcol + tid;
+        if (j < g.N) b[j] = __half_as_ushort(__float2half_rn((float)ls_scale<kScaleFp16>(nsum, dsum)));
+      }
+      if (tid == 0) counters[tile] = 0u;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ pack
+
+// One thread per (row, 16 columns): exact codes, 8 bytes out.
+template <int WT, int GRID, int AFMT, int G>
+__global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, int64_t ldw,
+                                                   int64_t M, int64_t N, const void* __restrict__ a_,
+                                                   const uint16_t* __restrict__ b,
+                                                   uint8_t* __restrict__ packed) {
+  using AT = typename ScaleStore<AFMT>::T;
+  const int64_t nch = N / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * nch) return;
+  const int64_t row = idx / nch, col = (idx - row * nch) * 16;
+  const float av = decode_scale<AFMT>(reinterpret_cast<const AT*>(a_)[row * (N / G) + col / G]);
+  const float ra = 1.0f / av;
+  float w[16];
+  load8<WT>(W, row * ldw + col, w);
+  load8<WT>(W, row * ldw + col + 8, w + 8);
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float bj = fp16_bits_to_float(b[col + k]);
+    const float q = Grid<GRID>::exact(w[k] * (1.0f / bj) * ra, w[k], av, bj);
+    word[k >> 3] |= Grid<GRID>::nibble(q) << (4 * (k & 7));
+  }
+  *reinterpret_cast<uint2*>(packed + row * (N / 2) + col / 2) = make_uint2(word[0], word[1]);
+}
+
+// ------------------------------------------------------- activation side
+
+// One thread per (token, block): X' = X D_b (exact in float32 for bf16 X),
+// s = Pi(absmax / qmax), codes = q(X' / s).
+template <int GRID, int AFMT, int G>
+__global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                        int64_t T, int64_t N,
+                                                        const uint16_t* __restrict__ b,
+                                                        uint8_t* __restrict__ xq,
+                                                        void* __restrict__ xs_) {
+  using AT = typename ScaleStore<AFMT>::T;
+  const int64_t nblk = N / G;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * nblk) return;
+  const int64_t t = idx / nblk, col = (idx - t * nblk) * G;
+  float x[G];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < G / 8; ++c) {
+    load8<kWBF16>(X, t * ldx + col + 8 * c, &x[8 * c]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x[8 * c + k] *= fp16_bits_to_float(b[col + 8 * c + k]);  // exact product
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(x[8 * c + k]));
+    }
+  }
+  const double s = amax > 0.0f ? project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0;
+  const float sf = (float)s, rs = 1.0f / sf;
+  uint32_t word[G / 8];
+#pragma unroll
+  for (int c = 0; c < G / 8; ++c) {
+    word[c] = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float q = Grid<GRID>::exact(x[8 * c + k] * rs, x[8 * c + k], sf, 1.0f);
+      word[c] |= Grid<GRID>::nibble(q) << (4 * k);
+    }
+  }
+  uint8_t* dst = xq + t * (N / 2) + col / 2;
+#pragma unroll
+  for (int c = 0; c < G / 8; ++c) reinterpret_cast<uint32_t*>(dst)[c] = word[c];
+  reinterpret_cast<AT*>(xs_)[idx] = encode_scale<AFMT>(s);
+}
+
+// ------------------------------------------------------------- launchers
+
+static inline unsigned blocks_for(int64_t n, int threads) {
+  return (unsigned)((n + threads - 1) / threads);
+}
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
+                       hipStream_t st) {
+  const int64_t n = max(M * (N / G), N);
+  init_rtn_kernel<WT, GRID, AFMT, G><<<blocks_for(n, 256), 256, 0, st>>>(W, ldw, M, N, a, b);
+  return hipGetLastError();
+}
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, uint32_t* counters,
+                          const PassGeom& g, int n_iters, hipStream_t st) {
+  fill_u32_kernel<<<blocks_for(g.n_tiles, 256), 256, 0, st>>>(counters, g.n_tiles, 0u);
+  hipError_t err = hipGetLastError();
+  for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
+    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, part, counters, g);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
+                       const uint16_t* b, uint8_t* packed, hipStream_t st) {
+  pack_kernel<WT, GRID, AFMT, G><<<blocks_for(M * (N / 16), 256), 256, 0, st>>>(W, ldw, M, N, a, b,
+                                                                              packed);
+  return hipGetLastError();
+}
+
+template <int GRID, int AFMT, int G>
+hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, const uint16_t* b,
+                      uint8_t* xq, void* xs, hipStream_t st) {
+  act_quant_kernel<GRID, AFMT, G><<<blocks_for(T * (N / G), 256), 256, 0, st>>>(X, ldx, T, N, b, xq,
+                                                                              xs);
+  return hipGetLastError();
+}
+
+// Explicit instantiation of every supported (weight type, grid, scale
+// format, group) combination.
+#define DQ_INST_WGA(WT, GR, AF, G)                                                               \
+  template hipError_t launch_init<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, void*,  \
+                                                 uint16_t*, hipStream_t);                         \
+  template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
+                                                    uint32_t*, const PassGeom&, int, hipStream_t); \
+  template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
+                                                 const void*, const uint16_t*, uint8_t*,          \
+                                                 hipStream_t);
+#define DQ_INST_GA(GR, AF, G)                                                                    \
+  DQ_INST_WGA(kWF32, GR, AF, G)                                                                  \
+  DQ_INST_WGA(kWBF16, GR, AF, G)                                                                 \
+  template hipError_t launch_act<GR, AF, G>(const uint16_t*, int64_t, int64_t, int64_t,          \
+                                            const uint16_t*, uint8_t*, void*, hipStream_t);
+#define DQ_INST_A(GR, AF) DQ_INST_GA(GR, AF, 16) DQ_INST_GA(GR, AF, 32) DQ_INST_GA(GR, AF, 64)
+#define DQ_INST(GR) DQ_INST_A(GR, kScaleFp16) DQ_INST_A(GR, kScaleE8M0) DQ_INST_A(GR, kScaleE4M3)
+
+#ifndef DQ_GRID_INST
+DQ_INST(kGridInt4)
+DQ_INST(kGridE2M1)
+#else
+DQ_INST(DQ_GRID_INST)
+#endif
+
+}  // namespace dq
