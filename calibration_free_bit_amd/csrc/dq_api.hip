@@ -39,7 +39,7 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 struct Workspace {
   PassGeom g;
-  size_t counter_off, bytes;
+  size_t bytes;
 };
 
 Workspace pass_geometry(const dq_problem* p) {
@@ -58,9 +58,7 @@ Workspace pass_geometry(const dq_problem* p) {
     const int64_t first = (t * g.S) / g.L, last = ((t + 1) * g.S - 1) / g.L;
     g.max_seg = std::max(g.max_seg, last - first + 1);
   }
-  const size_t part_bytes = size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double);
-  w.counter_off = align256(part_bytes);
-  w.bytes = w.counter_off + align256(size_t(g.n_tiles) * sizeof(uint32_t));
+  w.bytes = align256(size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double));
   return w;
 }
 
@@ -141,10 +139,9 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
   if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return DQ_ERR_WORKSPACE;
   double* part = static_cast<double*>(workspace);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws.counter_off);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
-    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, counters, ws.g, n_iters, st));
+    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, st));
   });
 }
 

@@ -202,4 +202,41 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* out
   }
 }
 
+// One lane's LC contiguous elements of a row, as raw 16-byte vectors.
+template <int WT, int LC> struct RawRow;
+
+template <int LC> struct RawRow<kWBF16, LC> {
+  uint4 v[LC / 8];
+  __device__ __forceinline__ void load(const void* base, int64_t elem) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < LC / 8; ++i) v[i] = p[i];
+  }
+  __device__ __forceinline__ void unpack(float* out) const {
+#pragma unroll
+    for (int i = 0; i < LC / 8; ++i) {
+      out[8 * i + 0] = bf16_lo(v[i].x); out[8 * i + 1] = bf16_hi(v[i].x);
+      out[8 * i + 2] = bf16_lo(v[i].y); out[8 * i + 3] = bf16_hi(v[i].y);
+      out[8 * i + 4] = bf16_lo(v[i].z); out[8 * i + 5] = bf16_hi(v[i].z);
+      out[8 * i + 6] = bf16_lo(v[i].w); out[8 * i + 7] = bf16_hi(v[i].w);
+    }
+  }
+};
+
+template <int LC> struct RawRow<kWF32, LC> {
+  float4 v[LC / 4];
+  __device__ __forceinline__ void load(const void* base, int64_t elem) {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int i = 0; i < LC / 4; ++i) v[i] = p[i];
+  }
+  __device__ __forceinline__ void unpack(float* out) const {
+#pragma unroll
+    for (int i = 0; i < LC / 4; ++i) {
+      out[4 * i + 0] = v[i].x; out[4 * i + 1] = v[i].y;
+      out[4 * i + 2] = v[i].z; out[4 * i + 3] = v[i].w;
+    }
+  }
+};
+
 }  // namespace dq

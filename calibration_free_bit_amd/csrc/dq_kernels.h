@@ -10,7 +10,10 @@ namespace dq {
 constexpr int kTileCols = 64;   // columns of one independent tile
 constexpr int kLaneCols = 16;   // contiguous columns one lane owns
 constexpr int kRowsPerStep = 4 * 64 * kLaneCols / kTileCols;  // rows per workgroup step
-constexpr int kPassGrid = 512;  // target workgroups of one BCD pass
+#ifndef DQ_PASS_GRID
+#define DQ_PASS_GRID 512
+#endif
+constexpr int kPassGrid = DQ_PASS_GRID;  // target workgroups of one BCD pass
 
 // Geometry of one BCD pass. Work is the flattened list of (tile, row step)
 // pairs, tile-major; workgroup w owns steps [w L, (w+1) L). The workgroups
@@ -25,16 +28,15 @@ struct PassGeom {
   int64_t n_wg;     // workgroups launched
   int64_t max_seg;  // most segments any tile has
 };
-// Workspace: part [n_tiles][max_seg][64][2] float64 column partial sums,
-// then counters [n_tiles] uint32 (zero between passes).
+// Workspace: part [n_tiles][max_seg][64][2] float64 column partial sums.
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                        hipStream_t st);
 
 template <int WT, int GRID, int AFMT, int G>
-hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, uint32_t* counters,
-                          const PassGeom& g, int n_iters, hipStream_t st);
+hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
+                          int n_iters, hipStream_t st);
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,

@@ -15,10 +15,11 @@
 // row, keeps those elements in registers between the two requantizations,
 // and accumulates float64 column sums for its columns across the rows it
 // visits. At the end of its range the workgroup
-// reduces those sums through LDS, writes one partial per column, and the
-// last workgroup to finish a tile (atomic counter) adds the partials in a
-// fixed order and writes b'. Q is never stored: it is recomputed from
-// (W, a, b) whenever needed, so one iteration reads W once.
+// reduces those sums through LDS and writes one partial per column; a small
+// second kernel adds the partials of each column in a fixed order and writes
+// b' (the kernel boundary makes the partials visible; no fences or
+// atomics). Q is never stored: it is recomputed from (W, a, b) whenever
+// needed, so one iteration reads W once.
 //
 // Every sum of the least-squares updates is accumulated in float64 in a
 // fixed order: each product is exact and, for bf16 weights, every partial
@@ -32,13 +33,6 @@ namespace dq {
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
-}
-
-// ------------------------------------------------------------ small fills
-
-static __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
 }
 
 // ------------------------------------------------------------------ init
@@ -70,11 +64,14 @@ __global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ 
 // ------------------------------------------------------------ BCD pass
 
 constexpr int kThreads = 256;  // 4 waves
+#ifndef DQ_PASS_OCC
+#define DQ_PASS_OCC 2  // workgroups per CU the register budget must allow
+#endif
 
 template <int WT, int GRID, int AFMT, int G>
-__global__ void __launch_bounds__(kThreads, 2)
-    bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, uint16_t* __restrict__ b,
-                    double* __restrict__ part, uint32_t* __restrict__ counters, PassGeom g) {
+__global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
+    bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, const uint16_t* __restrict__ b,
+                    double* __restrict__ part, PassGeom g) {
   using AT = typename ScaleStore<AFMT>::T;
   constexpr int LC = kLaneCols;             // contiguous columns per lane
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
@@ -85,11 +82,11 @@ __global__ void __launch_bounds__(kThreads, 2)
   constexpr int LPB = G > LC ? G / LC : 1;  // lanes sharing one block
   constexpr int kRedStride = RPS + 1;       // LDS pitch (doubles) of the reduction
   static_assert(RPS == kRowsPerStep, "geometry mismatch");
+  static_assert(LC == 16, "a lane's columns are all in range or all out (N % 16 == 0)");
 
   __shared__ float s_b[kTileCols];
   __shared__ float s_rb[kTileCols];
   __shared__ double s_red[kTileCols * kRedStride];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -120,29 +117,46 @@ __global__ void __launch_bounds__(kThreads, 2)
 #pragma unroll
     for (int e = 0; e < LC; ++e) { cn[e] = 0.0; cd[e] = 0.0; }
 
+    // Raw loads of one row step, issued one step ahead of their use. Out of
+    // range rows / columns read a clamped (valid) address; their values are
+    // zeroed before use.
+    const bool lane_cols_ok = col0 < g.N;  // the lane's 16 columns (N % 16 == 0)
+    RawRow<WT, LC> raw;
+    AT a_raw[NB];
+    auto issue = [&](int64_t step) {
+      const int64_t row = step * RPS + wave * RPW + rl;
+      const int64_t r = min(row, g.M - 1);
+      const int64_t c = lane_cols_ok ? col0 : 0;
+      raw.load(W, r * g.ldw + c);
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) a_raw[bl] = a[r * nblk + (c + bl * BL) / G];
+    };
+    issue(f - tile * g.S);
+
     for (; f < seg_end; ++f) {
-      const int64_t row = (f - tile * g.S) * RPS + wave * RPW + rl;
+      const int64_t step = f - tile * g.S;
+      const int64_t row = step * RPS + wave * RPW + rl;
       const bool row_ok = row < g.M;
+      // tiles past N exist only when N % 64 != 0; rows past M only in the last step
+      const bool full = (step + 1) * RPS <= g.M && tcol + kTileCols <= g.N;
 
       float w[LC];
-#pragma unroll
-      for (int c = 0; c < LC / 8; ++c) {
-        if (row_ok && col0 + 8 * c < g.N) {
-          load8<WT>(W, row * g.ldw + col0 + 8 * c, &w[8 * c]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) w[8 * c + k] = 0.0f;
-        }
-      }
-
+      raw.unpack(w);
       float a_old[NB];
       bool blk_ok[NB];
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) {
-        const int64_t c = col0 + bl * BL;
-        blk_ok[bl] = row_ok && c < g.N;
-        a_old[bl] = blk_ok[bl] ? decode_scale<AFMT>(a[row * nblk + c / G]) : 1.0f;
+        blk_ok[bl] = row_ok && lane_cols_ok;
+        a_old[bl] = decode_scale<AFMT>(a_raw[bl]);
       }
+      if (!full) {
+        const bool ok = row_ok && lane_cols_ok;
+#pragma unroll
+        for (int e = 0; e < LC; ++e) w[e] = ok ? w[e] : 0.0f;
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) a_old[bl] = ok ? a_old[bl] : 1.0f;
+      }
+      if (f + 1 < seg_end) issue(step + 1);
 
       // Q1 = q(W / (a b)) with the current state, fused with the row/block
       // least-squares sums (R = Q1 D_b). If any element of the wave lies
@@ -252,29 +266,34 @@ __global__ void __launch_bounds__(kThreads, 2)
       __syncthreads();
     }
 
-    // ---- last workgroup of the tile: b' = Pi_fp16(sum num / sum den)
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = atomicAdd(&counters[tile], 1u);
-      s_last = (int64_t)old == n_seg - 1;
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      if (tid < kTileCols) {
-        const double* pt = part + tile * g.max_seg * (kTileCols * 2) + tid * 2;
-        double nsum = 0.0, dsum = 0.0;
-        for (int64_t s = 0; s < n_seg; ++s) {
-          nsum += pt[s * (kTileCols * 2)];
-          dsum += pt[s * (kTileCols * 2) + 1];
-        }
-        const int64_t j = tcol + tid;
-        if (j < g.N) b[j] = __half_as_ushort(__float2half_rn((float)ls_scale<kScaleFp16>(nsum, dsum)));
+  }
+}
+
+// Column update: b' = Pi_fp16(sum num / sum den) over the segments of each
+// tile, added in segment order. One thread per column.
+static __global__ void __launch_bounds__(kTileCols)
+    bcd_column_kernel(const double* __restrict__ part, uint16_t* __restrict__ b, PassGeom g) {
+  const int64_t tile = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t first_wg = (tile * g.S) / g.L;
+  const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
+  const double2* pt = reinterpret_cast<const double2*>(part + tile * g.max_seg * (kTileCols * 2)) + tid;
+  double nsum = 0.0, dsum = 0.0;
+  for (int64_t s0 = 0; s0 < n_seg; s0 += 8) {  // 8 loads in flight, sums in order
+    double2 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = s0 + k < n_seg ? pt[(s0 + k) * kTileCols] : make_double2(0.0, 0.0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < n_seg) {
+        nsum += v[k].x;
+        dsum += v[k].y;
       }
-      if (tid == 0) counters[tile] = 0u;
     }
   }
+  const int64_t j = tile * kTileCols + tid;
+  if (j < g.N) b[j] = __half_as_ushort(__float2half_rn((float)ls_scale<kScaleFp16>(nsum, dsum)));
 }
 
 // ------------------------------------------------------------------ pack
@@ -364,12 +383,12 @@ hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a
 }
 
 template <int WT, int GRID, int AFMT, int G>
-hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, uint32_t* counters,
-                          const PassGeom& g, int n_iters, hipStream_t st) {
-  fill_u32_kernel<<<blocks_for(g.n_tiles, 256), 256, 0, st>>>(counters, g.n_tiles, 0u);
-  hipError_t err = hipGetLastError();
+hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
+                          int n_iters, hipStream_t st) {
+  hipError_t err = hipSuccess;
   for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
-    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, part, counters, g);
+    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, part, g);
+    bcd_column_kernel<<<(unsigned)g.n_tiles, kTileCols, 0, st>>>(part, b, g);
     err = hipGetLastError();
   }
   return err;
@@ -397,7 +416,7 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
   template hipError_t launch_init<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, void*,  \
                                                  uint16_t*, hipStream_t);                         \
   template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
-                                                    uint32_t*, const PassGeom&, int, hipStream_t); \
+                                                    const PassGeom&, int, hipStream_t);            \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
                                                  const void*, const uint16_t*, uint8_t*,          \
                                                  hipStream_t);
