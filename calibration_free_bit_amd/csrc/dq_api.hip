@@ -58,7 +58,8 @@ Workspace pass_geometry(const dq_problem* p) {
     const int64_t first = (t * g.S) / g.L, last = ((t + 1) * g.S - 1) / g.L;
     g.max_seg = std::max(g.max_seg, last - first + 1);
   }
-  w.bytes = align256(size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double));
+  // two alternating buffers of [n_tiles][max_seg][64][2] float64 partials
+  w.bytes = align256(2 * size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double));
   return w;
 }
 

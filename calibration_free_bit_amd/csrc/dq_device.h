@@ -115,6 +115,45 @@ __device__ __forceinline__ double ls_scale(double num, double den) {
   return den > 0.0 ? project<AFMT>(num / den) : 1.0;
 }
 
+// Fast path of ls_scale, in float32. The quotient num/den is formed from
+// the float32 roundings of num and den and a 1-ulp reciprocal, so it is
+// within 5 * 2^-24 (relative) of the exact quotient; the projection of that
+// approximation is the projection of the exact quotient unless it lies
+// within kScaleSure (relative) of a rounding boundary of the scale format,
+// in which case `unsure` is set and the caller must use ls_scale.
+constexpr float kScaleSure = 0x1p-20f;
+
+template <int AFMT>
+__device__ __forceinline__ float ls_scale_fast(double num, double den, bool& unsure) {
+  if (!(den > 0.0)) return 1.0f;
+  const float nf = (float)num, df = (float)den;
+  const float qf = nf * __builtin_amdgcn_rcpf(df);
+  // far outside every format's range, or denormal operands: exact path
+  if (!(qf > 0x1p-100f && qf < 0x1p100f) || !(df > 0x1p-100f)) {
+    unsure = true;
+    return 1.0f;
+  }
+  if constexpr (AFMT == kScaleE8M0) {
+    const float x = __builtin_fmaxf(qf, 0x1p-127f);
+    const int k = __builtin_amdgcn_frexp_expf(x) - 1;           // 2^k <= x < 2^(k+1)
+    const float mid = __builtin_ldexpf(1.5f, k);
+    unsure |= __builtin_fabsf(x - mid) <= kScaleSure * x;
+    return __builtin_ldexpf(1.0f, min(x >= mid ? k + 1 : k, 127));
+  } else {
+    constexpr float lo = AFMT == kScaleFp16 ? 0x1p-24f : 0x1p-9f;
+    constexpr float hi = AFMT == kScaleFp16 ? 65504.0f : 448.0f;
+    constexpr int kmin = AFMT == kScaleFp16 ? -14 : -6;           // smallest normal binade
+    constexpr int mbits = AFMT == kScaleFp16 ? 10 : 3;            // fraction bits
+    const float x = __builtin_fminf(__builtin_fmaxf(qf, lo), hi);
+    const int k = max(__builtin_amdgcn_frexp_expf(x) - 1, kmin);
+    const float c = __builtin_ldexpf(1.5f, k - mbits + 23);      // ulp of x + c is 2^(k-mbits)
+    const float r = (x + c) - c;                                 // nearest, ties to even
+    const float h = __builtin_ldexpf(1.0f, k - mbits - 1);       // half a step
+    unsure |= h - __builtin_fabsf(x - r) <= kScaleSure * x;
+    return r;
+  }
+}
+
 // ------------------------------------------------------- element quantizer
 
 template <int GRID> struct Grid;

@@ -28,7 +28,8 @@ struct PassGeom {
   int64_t n_wg;     // workgroups launched
   int64_t max_seg;  // most segments any tile has
 };
-// Workspace: part [n_tiles][max_seg][64][2] float64 column partial sums.
+// Workspace: two alternating [n_tiles][max_seg][64][2] float64 buffers of
+// column partial sums.
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,

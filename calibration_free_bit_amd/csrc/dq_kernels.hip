@@ -14,11 +14,12 @@
 // of row steps of a tile: every lane owns kLaneCols contiguous columns of one
 // row, keeps those elements in registers between the two requantizations,
 // and accumulates float64 column sums for its columns across the rows it
-// visits. At the end of its range the workgroup
-// reduces those sums through LDS and writes one partial per column; a small
-// second kernel adds the partials of each column in a fixed order and writes
-// b' (the kernel boundary makes the partials visible; no fences or
-// atomics). Q is never stored: it is recomputed from (W, a, b) whenever
+// visits. At the end of its range the workgroup reduces those sums through
+// LDS and writes one partial per column. The column update b' is formed by
+// the NEXT pass: each of its workgroups adds the partials of its tile in a
+// fixed order (the kernel boundary makes them visible; no fences or
+// atomics), and a small kernel writes b after the last pass. Partials
+// alternate between two buffers so a pass never overwrites what it reads. Q is never stored: it is recomputed from (W, a, b) whenever
 // needed, so one iteration reads W once.
 //
 // Every sum of the least-squares updates is accumulated in float64 in a
@@ -26,10 +27,19 @@
 // sum is exact, so the result does not depend on the order at all.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "dq_device.h"
 #include "dq_kernels.h"
 
 namespace dq {
+
+// Hide a value from the optimizer so that work derived from it is redone
+// where it is needed instead of being kept live in registers.
+template <class T>
+__device__ __forceinline__ void opaque(T& v) {
+  asm volatile("" : "+v"(v));
+}
 
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
@@ -64,14 +74,54 @@ __global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ 
 // ------------------------------------------------------------ BCD pass
 
 constexpr int kThreads = 256;  // 4 waves
+#ifndef DQ_PREFETCH
+#define DQ_PREFETCH 1
+#endif
+constexpr int kPrefetch = DQ_PREFETCH;  // row steps in flight per lane
+#ifndef DQ_RECONVERT_W
+#define DQ_RECONVERT_W 1
+#endif
+#ifndef DQ_ROW_CHAINS
+#define DQ_ROW_CHAINS 1  // independent partial sums per block in the row update
+#endif
+#ifndef DQ_B_IN_REGS
+#define DQ_B_IN_REGS 0
+#endif
 #ifndef DQ_PASS_OCC
 #define DQ_PASS_OCC 2  // workgroups per CU the register budget must allow
 #endif
 
+// Column update from the partials of one pass: b'_j = Pi_fp16(sum num /
+// sum den) over the segments of column j's tile, added in segment order.
+__device__ __forceinline__ float column_scale(const double* __restrict__ part, const PassGeom& g,
+                                              int64_t tile, int col) {
+  const int64_t first_wg = (tile * g.S) / g.L;
+  const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
+  const double2* pt = reinterpret_cast<const double2*>(part + tile * g.max_seg * (kTileCols * 2)) + col;
+  double nsum = 0.0, dsum = 0.0;
+  for (int64_t s0 = 0; s0 < n_seg; s0 += 8) {  // 8 loads in flight, sums in order
+    double2 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      v[k] = s0 + k < n_seg ? pt[(s0 + k) * kTileCols] : make_double2(0.0, 0.0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k < n_seg) {
+        nsum += v[k].x;
+        dsum += v[k].y;
+      }
+    }
+  }
+  return (float)ls_scale<kScaleFp16>(nsum, dsum);
+}
+
+// One BCD iteration. b of the state comes from the partial column sums of
+// the previous pass (part_in) when there is one, else from b in memory;
+// this pass's partial column sums go to part_out.
 template <int WT, int GRID, int AFMT, int G>
 __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, const uint16_t* __restrict__ b,
-                    double* __restrict__ part, PassGeom g) {
+                    const double* __restrict__ part_in, double* __restrict__ part_out, PassGeom g) {
   using AT = typename ScaleStore<AFMT>::T;
   constexpr int LC = kLaneCols;             // contiguous columns per lane
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
@@ -81,6 +131,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   constexpr int NB = LC / BL;               // blocks (or block parts) per lane
   constexpr int LPB = G > LC ? G / LC : 1;  // lanes sharing one block
   constexpr int kRedStride = RPS + 1;       // LDS pitch (doubles) of the reduction
+  constexpr int EB = WT == kWBF16 ? 2 : 4;  // bytes per W element
   static_assert(RPS == kRowsPerStep, "geometry mismatch");
   static_assert(LC == 16, "a lane's columns are all in range or all out (N % 16 == 0)");
 
@@ -100,98 +151,132 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     const int64_t tile = f / g.S;
     const int64_t seg_end = min(f_end, (tile + 1) * g.S);
     const int64_t tcol = tile * kTileCols;
+    const int64_t col0 = tcol + sub * LC;
+    const bool lane_cols_ok = col0 < g.N;
+    const int64_t ccol = lane_cols_ok ? col0 : 0;  // clamped column for loads
+
+    // Raw loads of row steps, issued kPrefetch steps ahead of their use
+    // (a ring of register buffers). Rows past M (last step of a tile) read
+    // row M-1; out of range values are zeroed before use.
+    RawRow<WT, LC> raw[kPrefetch];
+    AT a_raw[kPrefetch][NB];
+    auto issue = [&](int64_t st, int slot) {
+      const int64_t r = min(st * RPS + wave * RPW + rl, g.M - 1);
+      raw[slot].load(W, r * g.ldw + ccol);
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[r * nblk + (ccol + bl * BL) / G];
+    };
+    int64_t step = f - tile * g.S;
+#pragma unroll
+    for (int d = 0; d < kPrefetch; ++d)
+      if (f + d < seg_end) issue(step + d, d);
 
     __syncthreads();  // LDS of the previous segment is no longer read
     if (tid < kTileCols) {
       const int64_t j = tcol + tid;
-      const float bj = j < g.N ? fp16_bits_to_float(b[j]) : 1.0f;
+      float bj = 1.0f;
+      if (j < g.N) bj = part_in ? column_scale(part_in, g, tile, tid) : fp16_bits_to_float(b[j]);
       s_b[tid] = bj;
       s_rb[tid] = 1.0f / bj;
     }
     __syncthreads();
 
-    const int64_t col0 = tcol + sub * LC;
     const float* lb = s_b + sub * LC;
     const float* lrb = s_rb + sub * LC;
+#if DQ_B_IN_REGS
+    float rb_b[LC], rb_rb[LC];
+#pragma unroll
+    for (int e = 0; e < LC; ++e) { rb_b[e] = lb[e]; rb_rb[e] = lrb[e]; }
+#define LB(e) rb_b[e]
+#define LRB(e) rb_rb[e]
+#else
+#define LB(e) lb[e]
+#define LRB(e) lrb[e]
+#endif
     double cn[LC], cd[LC];
 #pragma unroll
     for (int e = 0; e < LC; ++e) { cn[e] = 0.0; cd[e] = 0.0; }
 
-    // Raw loads of one row step, issued one step ahead of their use. Out of
-    // range rows / columns read a clamped (valid) address; their values are
-    // zeroed before use.
-    const bool lane_cols_ok = col0 < g.N;  // the lane's 16 columns (N % 16 == 0)
-    RawRow<WT, LC> raw;
-    AT a_raw[NB];
-    auto issue = [&](int64_t step) {
-      const int64_t row = step * RPS + wave * RPW + rl;
-      const int64_t r = min(row, g.M - 1);
-      const int64_t c = lane_cols_ok ? col0 : 0;
-      raw.load(W, r * g.ldw + c);
-#pragma unroll
-      for (int bl = 0; bl < NB; ++bl) a_raw[bl] = a[r * nblk + (c + bl * BL) / G];
-    };
-    issue(f - tile * g.S);
+    // W pointer (bytes) and block-scale index of this lane's row, advanced
+    // by one step of RPS rows at a time.
+    const int64_t wstep = (int64_t)RPS * g.ldw * EB;
+    const int64_t astep = (int64_t)RPS * nblk;
+    int64_t row = step * RPS + wave * RPW + rl;
+    const char* wp = reinterpret_cast<const char*>(W) + (row * g.ldw + ccol) * EB;
+    int64_t ai = row * nblk + ccol / G;
 
-    for (; f < seg_end; ++f) {
-      const int64_t step = f - tile * g.S;
-      const int64_t row = step * RPS + wave * RPW + rl;
+    // One row step; the ring slot is a compile-time constant so that no
+    // in-flight register is ever copied (the loop below is unrolled by
+    // kPrefetch).
+    auto row_step = [&]<int SLOT>() {
       const bool row_ok = row < g.M;
-      // tiles past N exist only when N % 64 != 0; rows past M only in the last step
+      // rows past M occur only in the last step of a tile, columns past N
+      // only in the last tile
       const bool full = (step + 1) * RPS <= g.M && tcol + kTileCols <= g.N;
 
       float w[LC];
-      raw.unpack(w);
+      raw[SLOT].unpack(w);
       float a_old[NB];
-      bool blk_ok[NB];
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        blk_ok[bl] = row_ok && lane_cols_ok;
-        a_old[bl] = decode_scale<AFMT>(a_raw[bl]);
-      }
+      for (int bl = 0; bl < NB; ++bl) a_old[bl] = decode_scale<AFMT>(a_raw[SLOT][bl]);
+      const bool ok = row_ok && lane_cols_ok;
       if (!full) {
-        const bool ok = row_ok && lane_cols_ok;
 #pragma unroll
         for (int e = 0; e < LC; ++e) w[e] = ok ? w[e] : 0.0f;
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) a_old[bl] = ok ? a_old[bl] : 1.0f;
       }
-      if (f + 1 < seg_end) issue(step + 1);
+      // refill this slot with the step kPrefetch ahead
+      if (f + kPrefetch < seg_end) {
+        if ((step + kPrefetch + 1) * RPS <= g.M) {  // that step is entirely inside M
+          raw[SLOT].load(wp + kPrefetch * wstep, 0);
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl) a_raw[SLOT][bl] = a[ai + kPrefetch * astep + bl * BL / G];
+        } else {
+          issue(step + kPrefetch, SLOT);
+        }
+      }
 
       // Q1 = q(W / (a b)) with the current state, fused with the row/block
       // least-squares sums (R = Q1 D_b). If any element of the wave lies
       // near a rounding midpoint the sums are redone with exact codes.
       double num[NB], den[NB];
       float flag = 0.0f;
-#pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        const float ra = __builtin_amdgcn_rcpf(a_old[bl]);
-        num[bl] = 0.0;
-        den[bl] = 0.0;
-#pragma unroll
-        for (int k = 0; k < BL; ++k) {
-          const int e = bl * BL + k;
-          const float q = Grid<GRID>::fast(w[e] * lrb[e] * ra, flag);
-          const double R = (double)(q * lb[e]);  // exact product
-          num[bl] = __builtin_fma((double)w[e], R, num[bl]);
-          den[bl] = __builtin_fma(R, R, den[bl]);
-        }
-      }
-      if (wave_any(flag > kTieFlag)) {
+      // The sums of a block run in DQ_ROW_CHAINS interleaved partial sums
+      // (more independent float64 chains in flight), combined pairwise.
+      auto row_sums = [&](auto code_of) {
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-          const float ra = __builtin_amdgcn_rcpf(a_old[bl]);
-          num[bl] = 0.0;
-          den[bl] = 0.0;
+          double pn[DQ_ROW_CHAINS], pd[DQ_ROW_CHAINS];
+#pragma unroll
+          for (int c = 0; c < DQ_ROW_CHAINS; ++c) { pn[c] = 0.0; pd[c] = 0.0; }
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            const float q = Grid<GRID>::exact(w[e] * lrb[e] * ra, w[e], a_old[bl], lb[e]);
-            const double R = (double)(q * lb[e]);
-            num[bl] = __builtin_fma((double)w[e], R, num[bl]);
-            den[bl] = __builtin_fma(R, R, den[bl]);
+            const double R = (double)(code_of(bl, e) * LB(e));  // exact product
+            pn[k % DQ_ROW_CHAINS] = __builtin_fma((double)w[e], R, pn[k % DQ_ROW_CHAINS]);
+            pd[k % DQ_ROW_CHAINS] = __builtin_fma(R, R, pd[k % DQ_ROW_CHAINS]);
           }
+#pragma unroll
+          for (int span = 1; span < DQ_ROW_CHAINS; span <<= 1)
+#pragma unroll
+            for (int c = 0; c + span < DQ_ROW_CHAINS; c += 2 * span) {
+              pn[c] += pn[c + span];
+              pd[c] += pd[c + span];
+            }
+          num[bl] = pn[0];
+          den[bl] = pd[0];
         }
+      };
+      {
+        float ra[NB];
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) ra[bl] = __builtin_amdgcn_rcpf(a_old[bl]);
+        row_sums([&](int bl, int e) { return Grid<GRID>::fast(w[e] * LRB(e) * ra[bl], flag); });
+        if (wave_any(flag > kTieFlag))
+          row_sums([&](int bl, int e) {
+            return Grid<GRID>::exact(w[e] * LRB(e) * ra[bl], w[e], a_old[bl], LB(e));
+          });
       }
 #pragma unroll
       for (int m = 1; m < LPB; m <<= 1) {  // blocks wider than a lane
@@ -201,12 +286,16 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 
       // project, synchronize the copy that assigns codes, store
       float a_new[NB];
+      bool unsure = false;
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        const double an = ls_scale<AFMT>(num[bl], den[bl]);
-        a_new[bl] = (float)an;
-        if (blk_ok[bl] && (sub % LPB) == 0) a[row * nblk + (col0 + bl * BL) / G] = encode_scale<AFMT>(an);
+      for (int bl = 0; bl < NB; ++bl) a_new[bl] = ls_scale_fast<AFMT>(num[bl], den[bl], unsure);
+      if (wave_any(unsure)) {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) a_new[bl] = (float)ls_scale<AFMT>(num[bl], den[bl]);
       }
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl)
+        if (ok && (sub % LPB) == 0) a[ai + bl * BL / G] = encode_scale<AFMT>((double)a_new[bl]);
 
       // Q2 = q(W / (a' b))
       float q[LC];
@@ -217,7 +306,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
         for (int k = 0; k < BL; ++k) {
           const int e = bl * BL + k;
-          q[e] = Grid<GRID>::fast(w[e] * lrb[e] * ra, flag);
+          q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra, flag);
         }
       }
       if (wave_any(flag > kTieFlag)) {
@@ -227,12 +316,17 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            q[e] = Grid<GRID>::exact(w[e] * lrb[e] * ra, w[e], a_new[bl], lb[e]);
+            q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra, w[e], a_new[bl], LB(e));
           }
         }
       }
 
-      // column least-squares sums, S = D_a' Q2
+      // column least-squares sums, S = D_a' Q2 (w is re-converted here rather
+      // than kept live as float64 since the row sums)
+#if DQ_RECONVERT_W
+#pragma unroll
+      for (int e = 0; e < LC; ++e) opaque(w[e]);
+#endif
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) {
 #pragma unroll
@@ -243,13 +337,26 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
           cd[e] = __builtin_fma(S, S, cd[e]);
         }
       }
-    }
+    };
+    auto advance = [&]() {
+      ++f;
+      ++step;
+      row += RPS;
+      wp += wstep;
+      ai += astep;
+      return f < seg_end;
+    };
+    auto run_slots = [&]<int... S>(std::integer_sequence<int, S...>) {
+      while (((row_step.template operator()<S>(), advance()) && ...)) {
+      }
+    };
+    run_slots(std::make_integer_sequence<int, kPrefetch>{});
 
     // ---- reduce the RPS row-lanes of each column, write this segment's partial
     const int64_t first_wg = (tile * g.S) / g.L;
     const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
     const int64_t seg = (int64_t)blockIdx.x - first_wg;
-    double* __restrict__ pw = part + (tile * g.max_seg + seg) * (kTileCols * 2);
+    double* __restrict__ pw = part_out + (tile * g.max_seg + seg) * (kTileCols * 2);
 #pragma unroll
     for (int qn = 0; qn < 2; ++qn) {
 #pragma unroll
@@ -269,31 +376,13 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   }
 }
 
-// Column update: b' = Pi_fp16(sum num / sum den) over the segments of each
-// tile, added in segment order. One thread per column.
+// Final column update of a dq_bcd_iterate call: writes b from the last
+// pass's partials. One thread per column.
 static __global__ void __launch_bounds__(kTileCols)
     bcd_column_kernel(const double* __restrict__ part, uint16_t* __restrict__ b, PassGeom g) {
   const int64_t tile = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t first_wg = (tile * g.S) / g.L;
-  const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
-  const double2* pt = reinterpret_cast<const double2*>(part + tile * g.max_seg * (kTileCols * 2)) + tid;
-  double nsum = 0.0, dsum = 0.0;
-  for (int64_t s0 = 0; s0 < n_seg; s0 += 8) {  // 8 loads in flight, sums in order
-    double2 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      v[k] = s0 + k < n_seg ? pt[(s0 + k) * kTileCols] : make_double2(0.0, 0.0);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k < n_seg) {
-        nsum += v[k].x;
-        dsum += v[k].y;
-      }
-    }
-  }
-  const int64_t j = tile * kTileCols + tid;
-  if (j < g.N) b[j] = __half_as_ushort(__float2half_rn((float)ls_scale<kScaleFp16>(nsum, dsum)));
+  const int64_t j = tile * kTileCols + threadIdx.x;
+  if (j < g.N) b[j] = __half_as_ushort(__float2half_rn(column_scale(part, g, tile, threadIdx.x)));
 }
 
 // ------------------------------------------------------------------ pack
@@ -385,10 +474,18 @@ hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
                           int n_iters, hipStream_t st) {
+  // partial buffers alternate between passes: pass k reads the partials of
+  // pass k-1 (its column update) and writes its own to the other buffer
+  const int64_t half = g.n_tiles * g.max_seg * kTileCols * 2;
   hipError_t err = hipSuccess;
   for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
-    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, part, g);
-    bcd_column_kernel<<<(unsigned)g.n_tiles, kTileCols, 0, st>>>(part, b, g);
+    const double* in = it == 0 ? nullptr : part + ((it - 1) & 1) * half;
+    double* out = part + (it & 1) * half;
+    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, in, out, g);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess && n_iters > 0) {
+    bcd_column_kernel<<<(unsigned)g.n_tiles, kTileCols, 0, st>>>(part + ((n_iters - 1) & 1) * half, b, g);
     err = hipGetLastError();
   }
   return err;

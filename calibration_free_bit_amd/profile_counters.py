@@ -1,0 +1,157 @@
+"""Collect the rocprofv3 evidence behind bench.py's roofline entry.
+
+Runs, each in its own rocprofv3 process:
+  1. --kernel-trace --stats of ``bench.py`` (per-kernel average durations);
+  2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of ``bench.py`` (HBM bytes per
+     dispatch, in KiB);
+  3. the same two counters for ``bench.py --copy-calibration``, a plain
+     device copy of 256 MiB, whose known bytes give the scale factors of
+     the two counters.
+and writes to OUT_DIR:
+  bcd_pass_<workload>_kernel_trace.md   kernel-trace summary
+  bcd_pass_counters.json                traffic per pass launch + factors
+  bcd_pass_<workload>_counters.md       the same, readable
+
+Usage (on a machine with the GPU; rocprofv3 on PATH):
+  python -m calibration_free_bit_amd.profile_counters OUT_DIR [--workload W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import subprocess
+import sys
+import tempfile
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def _rocprof(args, prog, tag, work, timeout=300):
+    out = os.path.join(work, tag)
+    cmd = ["rocprofv3", *args, "-d", out, "-o", "run", "--output-format", "csv", "--",
+           sys.executable, *prog]
+    env = dict(os.environ, TMPDIR="/tmp")
+    print("[profile]", " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, cwd="/tmp", env=env, capture_output=True, text=True, timeout=timeout)
+    if r.returncode not in (0,):
+        print(r.stdout[-2000:], r.stderr[-4000:], flush=True)
+        raise RuntimeError(f"rocprofv3 failed ({r.returncode}) for {tag}")
+    return out, " ".join(cmd)
+
+
+def _find(root, suffix):
+    for d, _, files in os.walk(root):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(d, f)
+    raise FileNotFoundError(f"{suffix} under {root}")
+
+
+def _counters(root, counter, name_has):
+    """Per-dispatch values of one counter, for kernels whose name contains
+    name_has (summed over the counter's dimensions)."""
+    per = defaultdict(float)
+    for r in csv.DictReader(open(_find(root, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("out_dir")
+    ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
+    args = ap.parse_args()
+    os.makedirs(args.out_dir, exist_ok=True)
+    sys.path.insert(0, ROOT)
+    import bench  # for the source hash and the workload definition
+    from calibration_free_bit_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    bench_args = [BENCH, "--workload", wl.name, "--no-cpu-baseline"]
+    work = tempfile.mkdtemp(prefix="dqprof_", dir="/tmp")
+
+    # 1. kernel trace
+    tr, tr_cmd = _rocprof(["--kernel-trace", "--stats"], bench_args + ["--steps", "5", "--warmup", "1"],
+                          "trace", work)
+    stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
+    lines = [f"# Kernel trace: BCD solver, workload {wl.name}", "",
+             "Command (from /tmp, TMPDIR=/tmp):", "", f"    {tr_cmd}", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} % |")
+    open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_kernel_trace.md"), "w").write(
+        "\n".join(lines) + "\n")
+
+    # 2./3. byte counters, each counter in its own run
+    res = {}
+    cmds = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d, c = _rocprof(["--pmc", counter], bench_args + ["--steps", "2", "--warmup", "1"],
+                        f"pass_{counter}", work, timeout=180)
+        res[("pass", counter)] = _counters(d, counter, "bcd_pass_kernel")
+        cmds[("pass", counter)] = c
+        d, c = _rocprof(["--pmc", counter], [BENCH, "--copy-calibration"], f"copy_{counter}", work,
+                        timeout=180)
+        vals = _counters(d, counter, "")
+        res[("copy", counter)] = vals
+        cmds[("copy", counter)] = c
+
+    copy_bytes = 256 << 20
+    # the copy kernel is the largest dispatch of the calibration run
+    f_copy = max(res[("copy", "FETCH_SIZE")]) * 1024.0
+    w_copy = max(res[("copy", "WRITE_SIZE")]) * 1024.0
+    fetch_factor = copy_bytes / f_copy
+    write_factor = copy_bytes / w_copy
+    pf = res[("pass", "FETCH_SIZE")]
+    pw = res[("pass", "WRITE_SIZE")]
+    fetch_kib = sum(pf) / len(pf)
+    write_kib = sum(pw) / len(pw)
+    traffic = fetch_kib * 1024.0 * fetch_factor + write_kib * 1024.0 * write_factor
+    M, N = wl.spec.rows, wl.spec.cols
+    from calibration_free_bit_amd import dq
+    fmt = dq.FORMATS[wl.fmt]
+    b_alg = bench.alg_bytes_per_elem(2 if wl.spec.dtype == "bf16" else 4,
+                                     2 if fmt.a_fmt == dq.SCALE_FP16 else 1, fmt.group, M)
+    rec = {
+        "workload": wl.name,
+        "source_hash": bench.kernel_source_hash(),
+        "kernel": "bcd_pass_kernel",
+        "dispatches": len(pf),
+        "fetch_kib_per_launch": fetch_kib,
+        "write_kib_per_launch": write_kib,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": f_copy / 1024.0,
+        "copy_write_kib": w_copy / 1024.0,
+        "fetch_factor": fetch_factor,
+        "write_factor": write_factor,
+        "traffic_bytes_per_launch": traffic,
+        "traffic_bytes_per_element": traffic / (M * N),
+        "commands": {f"{k[0]}_{k[1]}": v for k, v in cmds.items()},
+    }
+    json.dump(rec, open(os.path.join(args.out_dir, "bcd_pass_counters.json"), "w"), indent=2)
+    md = [f"# HBM byte counters: bcd_pass_kernel, workload {wl.name}", "",
+          f"Per pass launch (average of {len(pf)} dispatches): FETCH_SIZE {fetch_kib:.0f} KiB, "
+          f"WRITE_SIZE {write_kib:.0f} KiB.", "",
+          f"Calibration: a plain 256 MiB device copy reads FETCH_SIZE {f_copy / 1024:.0f} KiB and "
+          f"WRITE_SIZE {w_copy / 1024:.0f} KiB, so the factors are {fetch_factor:.4f} (fetch) and "
+          f"{write_factor:.4f} (write).", "",
+          f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per weight "
+          f"element (algorithmic: {b_alg:.4f}).", "",
+          "Commands (each from /tmp, TMPDIR=/tmp):", ""]
+    md += [f"    {v}" for v in cmds.values()]
+    open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()
