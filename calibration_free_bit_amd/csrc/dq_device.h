@@ -5,8 +5,9 @@
 //   INT4  integers [-8, 7], round half to even, clip;
 //   E2M1  magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, nearest, ties to the even
 //         encoding, saturating at 6.
-// Scale sets (summary §3; reproduction README "Core equations": inverse
-// scales are projected onto hardware-legal values):
+// Scale sets (summary §3; reproduction README "Core equations": the
+// projection acts on inverse scales, since not every positive real can be
+// stored in the scale format):
 //   fp16  IEEE binary16, positive finite;
 //   E8M0  2^e, e in [-127, 127];
 //   E4M3  OCP E4M3FN without sign: k 2^-9 (k = 1..7) and 2^e (1 + m/8)

@@ -14,7 +14,7 @@
  *   a_i <- Pi_Fa(sum_j W_ij R_ij / sum_j R_ij^2),  R = Q D_b  (per block)
  *   b_j <- Pi_Fb(sum_i W_ij S_ij / sum_i S_ij^2),  S = D_a Q  (all rows)
  * each projected onto the format's legal scale values, with Q requantized
- * after each update and scale 1 for an all-zero code slice.
+ * after each update; a slice whose codes are all zero gets scale 1.
  *
  * Conventions for every call
  *  - All array arguments are DEVICE pointers owned by the caller. The

@@ -5,9 +5,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring). Plain float64 numpy.
 Sources
 -------
 * Element grids. [DQ summary] §3 "Quantization preliminaries": a value is
-  scaled, projected to the nearest representable value of the format and
-  rescaled; integer formats use round-and-clip, floating-point formats use
-  nearest-level projection on their non-uniform grid. The signed INT4
+  divided by its scale, sent to the closest value the format can hold, and
+  multiplied back; for integer grids that means rounding then clipping, for
+  floating-point grids picking the closest of the (unevenly spaced) levels.
+  The signed INT4
   codebook is [-8, 7] ([SQuant tutorial] Ch. 2 "Quantization from Scratch";
   [DQ repro] "Local reproduction"). The symmetric int8 range [-127, 127] is
   the one of the worked example in [SQuant tutorial] Ch. 2. NVFP4's element
@@ -15,8 +16,8 @@ Sources
   0, 0.5, 1, 1.5, 2, 3, 4, 6.
 * Scale sets. [DQ summary] §3: MX formats use E8M0 (power-of-two) block
   scales; NVFP4 uses FP8 UE4M3 block scales; INT4 uses fp16 scales here.
-  [DQ repro] "Core equations": projection is applied to the inverse scales,
-  because arbitrary positive reals are not necessarily hardware legal.
+  [DQ repro] "Core equations": the projection acts on the inverse scales,
+  since a scale format can store only some positive reals.
 
 Readings where the pages are silent (each is listed in the design doc):
 * integer rounding ties go to the even integer (``np.rint``);
@@ -167,8 +168,8 @@ def _nearest_index(x: np.ndarray, fmt: str) -> np.ndarray:
 def project(x: np.ndarray, fmt: str) -> np.ndarray:
     """Projection Pi_F onto the legal positive scale values of ``fmt``.
 
-    [DQ repro] "Core equations" and [DQ summary] App. B: each updated
-    inverse scale is projected to the nearest representable value.
+    [DQ repro] "Core equations" and [DQ summary] App. B: every updated
+    inverse scale is replaced by the closest value its format can hold.
     ``fmt`` is "fp16", "e8m0", "e4m3" or "f32" (identity).
     """
     x = np.asarray(x, dtype=np.float64)

@@ -2,8 +2,8 @@
 
 Element grids: [DQ summary] §3 (round-and-clip for integers, nearest level
 for floating-point grids); scale sets: [DQ summary] §3 (fp16 / E8M0 /
-UE4M3); projection: [DQ repro] "Core equations" (nearest representable
-inverse scale). Independent references used here: numpy's float16 cast,
+UE4M3); projection: [DQ repro] "Core equations" (closest storable inverse
+scale). Independent references used here: numpy's float16 cast,
 torch's float8_e4m3fn dtype, the E2M1 bit layout, and brute force over the
 whole legal set.
 """

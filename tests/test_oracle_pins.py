@@ -5,9 +5,9 @@ printed value, a brute-force search over the whole legal set, a textbook
 routine, an exact-rational re-run, or an invariant of the method.
 
 Passages: [DQ repro] "Core equations" (closed-form updates, projection,
-requantization after each update, scale 1 for an all-zero code slice);
+requantization after each update, scale 1 where a slice has only zero codes);
 [DQ summary] §3 (formats, absmax scale), §4.3 / App. B / App. C
-(monotone descent, nearest representable projection), App. I / Table 12
+(monotone descent, projection to the closest storable value), App. I / Table 12
 (packed footprint); [SQuant tutorial] Ch. 2 (worked int8 example);
 [RTN tutorial] "Round-to-Nearest (RTN)" (error bound s/2).
 """
