@@ -241,10 +241,11 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       // least-squares sums (R = Q1 D_b). If any element of the wave lies
       // near a rounding midpoint the sums are redone with exact codes.
       double num[NB], den[NB];
+      float q[LC];  // Q1 here; becomes Q2 below
       float flag = 0.0f;
       // The sums of a block run in DQ_ROW_CHAINS interleaved partial sums
       // (more independent float64 chains in flight), combined pairwise.
-      auto row_sums = [&](auto code_of) {
+      auto row_sums = [&]() {
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
           double pn[DQ_ROW_CHAINS], pd[DQ_ROW_CHAINS];
@@ -253,7 +254,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            const double R = (double)(code_of(bl, e) * LB(e));  // exact product
+            const double R = (double)(q[e] * LB(e));  // exact product
             pn[k % DQ_ROW_CHAINS] = __builtin_fma((double)w[e], R, pn[k % DQ_ROW_CHAINS]);
             pd[k % DQ_ROW_CHAINS] = __builtin_fma(R, R, pd[k % DQ_ROW_CHAINS]);
           }
@@ -272,11 +273,23 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         float ra[NB];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) ra[bl] = __builtin_amdgcn_rcpf(a_old[bl]);
-        row_sums([&](int bl, int e) { return Grid<GRID>::fast(w[e] * LRB(e) * ra[bl], flag); });
-        if (wave_any(flag > kTieFlag))
-          row_sums([&](int bl, int e) {
-            return Grid<GRID>::exact(w[e] * LRB(e) * ra[bl], w[e], a_old[bl], LB(e));
-          });
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+          for (int k = 0; k < BL; ++k) {
+            const int e = bl * BL + k;
+            q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra[bl], flag);
+          }
+        if (wave_any(flag > kTieFlag)) {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+            for (int k = 0; k < BL; ++k) {
+              const int e = bl * BL + k;
+              q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra[bl], w[e], a_old[bl], LB(e));
+            }
+        }
+        row_sums();
       }
 #pragma unroll
       for (int m = 1; m < LPB; m <<= 1) {  // blocks wider than a lane
@@ -297,26 +310,31 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       for (int bl = 0; bl < NB; ++bl)
         if (ok && (sub % LPB) == 0) a[ai + bl * BL / G] = encode_scale<AFMT>((double)a_new[bl]);
 
-      // Q2 = q(W / (a' b))
-      float q[LC];
-      flag = 0.0f;
+      // Q2 = q(W / (a' b)). Where no block scale of the wave changed, Q2 is
+      // Q1 (same quotient, same decision) and is not recomputed.
+      bool changed = false;
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) {
-        const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
-#pragma unroll
-        for (int k = 0; k < BL; ++k) {
-          const int e = bl * BL + k;
-          q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra, flag);
-        }
-      }
-      if (wave_any(flag > kTieFlag)) {
+      for (int bl = 0; bl < NB; ++bl) changed |= a_new[bl] != a_old[bl];
+      if (wave_any(changed)) {
+        flag = 0.0f;
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
           const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra, w[e], a_new[bl], LB(e));
+            q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra, flag);
+          }
+        }
+        if (wave_any(flag > kTieFlag)) {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl) {
+            const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
+#pragma unroll
+            for (int k = 0; k < BL; ++k) {
+              const int e = bl * BL + k;
+              q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra, w[e], a_new[bl], LB(e));
+            }
           }
         }
       }
