@@ -32,6 +32,9 @@ int check_problem(const dq_problem* p) {
   if (p->rows < 1 || p->cols < 1 || p->cols % p->group != 0) return DQ_ERR_SHAPE;
   if (p->ldw < p->cols || (p->ldw * elem_size(p->w_type)) % 16 != 0) return DQ_ERR_SHAPE;
   if (p->rows > (int64_t(1) << 40) / p->ldw) return DQ_ERR_SHAPE;  // keep offsets far from overflow
+  // the pass kernel's tile/step bookkeeping is 32-bit
+  if (ceil_div(p->rows, dq::kRowsPerStep) * ceil_div(p->cols, dq::kTileCols) >= (int64_t(1) << 31))
+    return DQ_ERR_SHAPE;
   return DQ_OK;
 }
 

@@ -93,26 +93,58 @@ constexpr int kPrefetch = DQ_PREFETCH;  // row steps in flight per lane
 
 // Column update from the partials of one pass: b'_j = Pi_fp16(sum num /
 // sum den) over the segments of column j's tile, added in segment order.
-__device__ __forceinline__ float column_scale(const double* __restrict__ part, const PassGeom& g,
-                                              int64_t tile, int col) {
-  const int64_t first_wg = (tile * g.S) / g.L;
-  const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
-  const double2* pt = reinterpret_cast<const double2*>(part + tile * g.max_seg * (kTileCols * 2)) + col;
-  double nsum = 0.0, dsum = 0.0;
-  for (int64_t s0 = 0; s0 < n_seg; s0 += 8) {  // 8 loads in flight, sums in order
-    double2 v[8];
+// Segment geometry of a tile: the first workgroup whose range touches it and
+// how many do. Every count here is below 2^31 (the host checks), so 32-bit
+// division is exact.
+__device__ __forceinline__ uint32_t tile_first_wg(const PassGeom& g, uint32_t tile) {
+  return (tile * (uint32_t)g.S) / (uint32_t)g.L;
+}
+__device__ __forceinline__ uint32_t tile_n_seg(const PassGeom& g, uint32_t tile) {
+  return ((tile + 1) * (uint32_t)g.S - 1) / (uint32_t)g.L - tile_first_wg(g, tile) + 1;
+}
+
+// The loads are split from the sums so that a caller can issue the first
+// batch early and overlap its latency with other loads.
+struct ColumnPartials {
+  static constexpr int kBatch = 8;  // loads in flight
+  const double2* pt;
+  int64_t n_seg;
+  double2 v[kBatch];
+
+  // An inactive instance loads nothing and sums to the empty sums.
+  __device__ __forceinline__ ColumnPartials(const double* __restrict__ part, const PassGeom& g,
+                                            int64_t tile, int col, bool active = true) {
+    n_seg = active ? tile_n_seg(g, (uint32_t)tile) : 0;
+    pt = active ? reinterpret_cast<const double2*>(part + tile * g.max_seg * (kTileCols * 2)) + col
+                : nullptr;
+    load(0);
+  }
+  __device__ __forceinline__ void load(int64_t s0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < kBatch; ++k)
       v[k] = s0 + k < n_seg ? pt[(s0 + k) * kTileCols] : make_double2(0.0, 0.0);
+  }
+  // sums in segment order, then the projected least-squares scale
+  __device__ __forceinline__ float finish() {
+    double nsum = 0.0, dsum = 0.0;
+    for (int64_t s0 = 0; s0 < n_seg; s0 += kBatch) {
+      if (s0 > 0) load(s0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k < n_seg) {
-        nsum += v[k].x;
-        dsum += v[k].y;
+      for (int k = 0; k < kBatch; ++k) {
+        if (s0 + k < n_seg) {
+          nsum += v[k].x;
+          dsum += v[k].y;
+        }
       }
     }
+    return (float)ls_scale<kScaleFp16>(nsum, dsum);
   }
-  return (float)ls_scale<kScaleFp16>(nsum, dsum);
+};
+
+__device__ __forceinline__ float column_scale(const double* __restrict__ part, const PassGeom& g,
+                                              int64_t tile, int col) {
+  ColumnPartials cp(part, g, tile, col);
+  return cp.finish();
 }
 
 // One BCD iteration. b of the state comes from the partial column sums of
@@ -130,10 +162,15 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   constexpr int BL = G < LC ? G : LC;       // elements of one block inside a lane
   constexpr int NB = LC / BL;               // blocks (or block parts) per lane
   constexpr int LPB = G > LC ? G / LC : 1;  // lanes sharing one block
-  constexpr int kRedStride = RPS + 1;       // LDS pitch (doubles) of the reduction
+  // LDS of the column reduction: row c' = e * LPR + sub holds the sums of
+  // column sub * LC + e from every row-lane. With this order and a pitch of
+  // 68 doubles the lanes of one store (same e) and of one load (rows r*4 + pi)
+  // spread over distinct banks.
+  constexpr int kRedStride = 68;
   constexpr int EB = WT == kWBF16 ? 2 : 4;  // bytes per W element
   static_assert(RPS == kRowsPerStep, "geometry mismatch");
   static_assert(LC == 16, "a lane's columns are all in range or all out (N % 16 == 0)");
+  static_assert(RPS == 64, "the reduction's LDS pitch assumes 64 row-lanes");
 
   __shared__ float s_b[kTileCols];
   __shared__ float s_rb[kTileCols];
@@ -148,7 +185,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   int64_t f = (int64_t)blockIdx.x * g.L;
   const int64_t f_end = min(f + g.L, g.total);
   while (f < f_end) {
-    const int64_t tile = f / g.S;
+    const int64_t tile = (uint32_t)f / (uint32_t)g.S;
     const int64_t seg_end = min(f_end, (tile + 1) * g.S);
     const int64_t tcol = tile * kTileCols;
     const int64_t col0 = tcol + sub * LC;
@@ -371,20 +408,20 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     run_slots(std::make_integer_sequence<int, kPrefetch>{});
 
     // ---- reduce the RPS row-lanes of each column, write this segment's partial
-    const int64_t first_wg = (tile * g.S) / g.L;
-    const int64_t n_seg = ((tile + 1) * g.S - 1) / g.L - first_wg + 1;
-    const int64_t seg = (int64_t)blockIdx.x - first_wg;
+    const int64_t seg = (int64_t)blockIdx.x - tile_first_wg(g, (uint32_t)tile);
     double* __restrict__ pw = part_out + (tile * g.max_seg + seg) * (kTileCols * 2);
 #pragma unroll
     for (int qn = 0; qn < 2; ++qn) {
 #pragma unroll
-      for (int e = 0; e < LC; ++e)
-        s_red[(sub * LC + e) * kRedStride + wave * RPW + rl] = qn ? cd[e] : cn[e];
+      for (int e = 0; e < LC; ++e) {
+        s_red[(e * LPR + sub) * kRedStride + wave * RPW + rl] = qn ? cd[e] : cn[e];
+      }
       __syncthreads();
-      const int c = tid >> 2, pi = tid & 3;
+      const int cr = tid >> 2, pi = tid & 3;  // LDS row, quarter of the row-lanes
       double acc = 0.0;
+      const int c = (cr % LPR) * LC + cr / LPR;  // the column of LDS row cr
 #pragma unroll 8
-      for (int r = 0; r < RPS / 4; ++r) acc += s_red[c * kRedStride + pi * (RPS / 4) + r];
+      for (int r = 0; r < RPS / 4; ++r) acc += s_red[cr * kRedStride + r * 4 + pi];
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
       if (pi == 0) pw[c * 2 + qn] = acc;
