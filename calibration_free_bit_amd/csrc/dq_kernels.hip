@@ -78,9 +78,6 @@ constexpr int kThreads = 256;  // 4 waves
 #define DQ_PREFETCH 1
 #endif
 constexpr int kPrefetch = DQ_PREFETCH;  // row steps in flight per lane
-#ifndef DQ_RECONVERT_W
-#define DQ_RECONVERT_W 1
-#endif
 #ifndef DQ_ROW_CHAINS
 #define DQ_ROW_CHAINS 1  // independent partial sums per block in the row update
 #endif
@@ -376,12 +373,13 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         }
       }
 
-      // column least-squares sums, S = D_a' Q2 (w is re-converted here rather
-      // than kept live as float64 since the row sums)
-#if DQ_RECONVERT_W
+      // column least-squares sums, S = D_a' Q2. The float64 copies of w made
+      // for the row sums stay live for bf16 weights; float32 weights need
+      // more registers, so there w is converted again.
+      if constexpr (WT == kWF32) {
 #pragma unroll
-      for (int e = 0; e < LC; ++e) opaque(w[e]);
-#endif
+        for (int e = 0; e < LC; ++e) opaque(w[e]);
+      }
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) {
 #pragma unroll

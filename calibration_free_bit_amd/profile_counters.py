@@ -32,6 +32,21 @@ ROOT = os.path.dirname(HERE)
 BENCH = os.path.join(ROOT, "bench.py")
 
 
+def _shown(cmd):
+    """The command as a reader reruns it: the repository as /root/repo, the
+    interpreter as python3, the output folder as OUT."""
+    txt = []
+    for c in cmd:
+        if c == sys.executable:
+            c = "python3"
+        elif c.startswith(ROOT):
+            c = "/root/repo" + c[len(ROOT):]
+        elif c.startswith("/tmp/dqprof_"):
+            c = "OUT/" + os.path.basename(c)
+        txt.append(c)
+    return "cd /tmp && export TMPDIR=/tmp && " + " ".join(txt)
+
+
 def _rocprof(args, prog, tag, work, timeout=300):
     out = os.path.join(work, tag)
     cmd = ["rocprofv3", *args, "-d", out, "-o", "run", "--output-format", "csv", "--",
@@ -42,7 +57,7 @@ def _rocprof(args, prog, tag, work, timeout=300):
     if r.returncode not in (0,):
         print(r.stdout[-2000:], r.stderr[-4000:], flush=True)
         raise RuntimeError(f"rocprofv3 failed ({r.returncode}) for {tag}")
-    return out, " ".join(cmd)
+    return out, _shown(cmd)
 
 
 def _find(root, suffix):
@@ -82,7 +97,7 @@ def main():
                           "trace", work)
     stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
     lines = [f"# Kernel trace: BCD solver, workload {wl.name}", "",
-             "Command (from /tmp, TMPDIR=/tmp):", "", f"    {tr_cmd}", "",
+             "Command:", "", f"    {tr_cmd}", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |",
              "|---|---:|---:|---:|---:|---:|"]
     for r in stats:
@@ -147,7 +162,7 @@ def main():
           f"{write_factor:.4f} (write).", "",
           f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per weight "
           f"element (algorithmic: {b_alg:.4f}).", "",
-          "Commands (each from /tmp, TMPDIR=/tmp):", ""]
+          "Commands:", ""]
     md += [f"    {v}" for v in cmds.values()]
     open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.md"), "w").write("\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
