@@ -14,7 +14,12 @@ and the column scales) over its average duration, measured with events on
 the stream the kernel runs on. cpu_baseline times the float64 oracle on
 the host (test infrastructure, never on the product path).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+With --workload llama31_8b_int4_g64_bf16 the step is instead the whole
+Llama-3.1-8B linear-layer set (32 layers x q, k, v, o, gate, up, down;
+6.98 G bf16 weights resident in HBM, INT4 G64, T = 20), every matrix solved
+(init, iterate, pack) with the matrices spread over --streams streams.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 from __future__ import annotations
@@ -103,12 +108,113 @@ def copy_calibration(nbytes: int = 256 << 20, reps: int = 3):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
 
 
+SET_WORKLOAD = "llama31_8b_int4_g64_bf16"
+
+
+def _make_set_matrix(item):
+    from calibration_free_bit_amd import synth
+    l, p, name, spec, seed = item
+    return l, p, synth.make_matrix(spec, seed).data
+
+
+def set_cpu_baseline(items, budget_s: float = 20.0):
+    """The float64 oracle on a bounded sample of the set: the first column
+    stripes of layer 0's matrices, as many as fit the budget."""
+    from oracle import dualquant as D
+    from calibration_free_bit_amd import synth
+    fmt = D.FORMATS["int4_g64"]
+    done, elems, t_used, parts = 0, 0, 0.0, []
+    for (l, p, name, spec, seed) in items[:7]:
+        if t_used > budget_s:
+            break
+        data = synth.make_matrix(spec, seed).data
+        W = synth.bf16_to_f64(data[:, :2 * fmt.group])
+        t0 = time.perf_counter()
+        D.solve(W, fmt, 20)
+        t_used += time.perf_counter() - t0
+        elems += W.size
+        parts.append(f"{name} {W.shape[0]}x{W.shape[1]}")
+    return {"value": elems * 20 / t_used, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": "float64 numpy oracle, first 2 column stripes of layer 0's " + ", ".join(parts)
+                      + f"; T=20, {t_used:.1f} s"}
+
+
+def run_set(args):
+    """The whole Llama-3.1-8B linear set on one GPU, spread over streams."""
+    import multiprocessing as mp
+    from calibration_free_bit_amd import synth
+    items = synth.llama_layer_specs()
+    # host generation in worker processes forked before the GPU is touched
+    n_proc = max(1, min(16, len(os.sched_getaffinity(0))))
+    pool = mp.get_context("fork").Pool(n_proc)
+    import numpy as np
+    import torch
+    from calibration_free_bit_amd import dq
+    fmt = dq.FORMATS["int4_g64"]
+    T = 20
+    t_gen = time.perf_counter()
+    solvers = [None] * len(items)
+    index = {(l, p): k for k, (l, p, _, _, _) in enumerate(items)}
+    for l, p, data in pool.imap_unordered(_make_set_matrix, items, chunksize=1):
+        W = torch.from_numpy(data.view(np.int16)).to("cuda:0")
+        solvers[index[(l, p)]] = dq.Solver(W, fmt)
+    pool.close()
+    pool.join()
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    elems = sum(s.W.numel() for s in solvers)
+    streams = [torch.cuda.Stream() for _ in range(args.streams)]
+    cur = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dq.solve_on_streams(solvers, T, streams)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(cur)
+    for _ in range(args.steps):
+        dq.solve_on_streams(solvers, T, streams)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / args.steps
+    value = elems * T / (step_ms * 1e-3)
+    b_alg = alg_bytes_per_elem(2, 2, fmt.group, 4096)
+    achieved = value * b_alg / 1e9  # whole step, init and pack included
+    out = {
+        "metric": "weight elements/s per BCD iteration",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32-requant/f64-sums",
+        "data": "synthetic (seeded, numpy PCG64)",
+        "config": {"workload": SET_WORKLOAD, "matrices": len(solvers), "elements": elems,
+                   "format": "int4_g64", "iters": T, "streams": args.streams,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "whole step (every kernel of the set, overlapped on streams)",
+                     "alg_bytes_per_elem": b_alg},
+        "breakdown_ms": {"wall_per_step": wall * 1e3 / args.steps, "host_generation_s": t_gen},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = set_cpu_baseline(items)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
+    ap.add_argument("--streams", type=int, default=4, help="streams of the Llama set workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (for scaling byte counters)")
@@ -121,6 +227,10 @@ def main():
               "the solver shards by column stripes with no communication, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == SET_WORKLOAD:
+        run_set(args)
+        return
 
     import numpy as np
     import torch

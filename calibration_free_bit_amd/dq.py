@@ -190,3 +190,29 @@ class Solver:
         self.init(stream)
         self.iterate(iters, stream)
         self.pack(stream)
+
+
+def assign_streams(sizes, n_streams: int):
+    """Greedy longest-first assignment of matrices (by element count) to
+    streams: returns the stream index of every matrix. Deterministic."""
+    load = [0] * n_streams
+    out = [0] * len(sizes)
+    for k in sorted(range(len(sizes)), key=lambda k: (-sizes[k], k)):
+        j = min(range(n_streams), key=lambda j: (load[j], j))
+        out[k] = j
+        load[j] += sizes[k]
+    return out
+
+
+def solve_on_streams(solvers, iters: int, streams) -> None:
+    """solve(iters) for every solver, the matrices spread over ``streams``
+    (forked from and joined back into the current stream), so that passes of
+    different matrices overlap on the device."""
+    cur = torch.cuda.current_stream()
+    where = assign_streams([s.W.shape[0] * s.W.shape[1] for s in solvers], len(streams))
+    for st in streams:
+        st.wait_stream(cur)
+    for s, j in zip(solvers, where):
+        s.solve(iters, streams[j])
+    for st in streams:
+        cur.wait_stream(st)

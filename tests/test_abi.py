@@ -11,7 +11,7 @@ import re
 
 import pytest
 
-from calibration_free_bit_amd import dq
+from calibration_free_bit_amd import dq, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -124,3 +124,13 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(dq, "LIB_PATH", "/nonexistent/libdq.so")
     with pytest.raises(RuntimeError, match="HIP library not found"):
         dq.lib()
+
+
+def test_assign_streams_is_balanced_and_deterministic():
+    # host-side scheduling of the set workload: greedy longest-first
+    sizes = [sp.rows * sp.cols for _, _, _, sp, _ in synth.llama_layer_specs()]
+    w = dq.assign_streams(sizes, 4)
+    assert w == dq.assign_streams(sizes, 4)
+    load = [sum(s for s, j in zip(sizes, w) if j == k) for k in range(4)]
+    assert max(load) - min(load) <= max(sizes)
+    assert dq.assign_streams([5, 3, 3, 1], 2) == [0, 1, 1, 0]

@@ -184,3 +184,29 @@ def test_full_size_sampled_stripes(wl_name):
     from oracle import formats as F
     np.testing.assert_array_equal(F.project(a.ravel(), ofmt.a_fmt), a.ravel())
     np.testing.assert_array_equal(F.project(b, "fp16"), b)
+
+
+def test_llama_layer_set_on_streams():
+    """Layer 0 of the Llama-3.1-8B linear set (all seven shapes of the set:
+    q, k, v, o, gate, up, down) solved together with the matrices spread over
+    four streams, as the set workload of the benchmark runs; every matrix is
+    checked on whole column stripes against the oracle."""
+    items = synth.llama_layer_specs()[:7]
+    fmt = dq.FORMATS["int4_g64"]
+    ofmt = oracle_fmt(fmt)
+    G = fmt.group
+    mats = [synth.make_matrix(spec, seed) for (_, _, _, spec, seed) in items]
+    print("[case] llama layer 0 on 4 streams, T=20", flush=True)
+    runs = [GpuRun(m.data, fmt) for m in mats]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    dq.solve_on_streams([r.s for r in runs], 20, streams)
+    torch.cuda.synchronize()
+    for (_, _, name, spec, _), m, g in zip(items, mats, runs):
+        a, b, Q = g.a, g.b, g.Q
+        n_str = spec.cols // G
+        for s in sorted({0, n_str - 1, int(m.outlier_cols[0]) // G}):
+            cs = slice(s * G, s * G + G)
+            Ws = synth.bf16_to_f64(m.data[:, cs])
+            sol = D.solve(Ws, ofmt, 20)
+            r = compare(Ws, a[:, s:s + 1], b[cs], Q[:, cs], sol, ofmt, f"{name} stripe {s}")
+            assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, (name, s, r)
