@@ -152,7 +152,8 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
 int dq_pack_codes(const dq_problem* p, const void* W, const void* a, const uint16_t* b,
                   uint8_t* packed, void* stream) {
   if (int s = check_problem(p)) return s;
-  if (!W || !a || !b || !packed || !aligned16(W) || (reinterpret_cast<uintptr_t>(packed) & 7u))
+  if (!W || !a || !b || !packed || !aligned16(W) || !aligned16(b) ||
+      (reinterpret_cast<uintptr_t>(packed) & 7u))
     return DQ_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
@@ -166,7 +167,8 @@ int dq_rescale_quantize_act(const dq_problem* p, const void* X, int64_t tokens, 
   if (p->w_type != DQ_W_BF16) return DQ_ERR_UNSUPPORTED;  // X' = X D_b is exact only for bf16 X
   if (tokens < 0 || ldx < p->cols || (ldx * 2) % 16 != 0) return DQ_ERR_SHAPE;
   if (tokens == 0) return DQ_OK;
-  if (!X || !b || !xq || !x_scales || !aligned16(X) || !aligned16(xq)) return DQ_ERR_INVALID_ARG;
+  if (!X || !b || !xq || !x_scales || !aligned16(X) || !aligned16(b) || !aligned16(xq))
+    return DQ_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* Xh = static_cast<const uint16_t*>(X);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {

@@ -182,6 +182,22 @@ template <> struct Grid<kGridInt4> {
   __device__ static __forceinline__ uint32_t nibble(float q) {
     return (uint32_t)((int)q) & 0xFu;
   }
+  // Codes of N estimates; true if any of them may round differently at the
+  // exact quotient (then the caller re-decides with exact()).
+  template <int N>
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q) {
+    float flag = 0.0f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) q[e] = fast(y[e], flag);
+    return flag > kTieFlag;
+  }
+  // Nibbles of 8 codes, element k in bits 4k..4k+3.
+  __device__ static __forceinline__ uint32_t pack8(const float* q) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w |= nibble(q[k]) << (4 * k);
+    return w;
+  }
 };
 
 template <> struct Grid<kGridE2M1> {
@@ -216,6 +232,56 @@ template <> struct Grid<kGridE2M1> {
                        : aq < 4.0f ? (uint32_t)aq + 2u
                        : (aq < 5.0f ? 6u : 7u);
     return idx | ((q < 0.0f) ? 8u : 0u);
+  }
+
+  // gfx950's scaled FP4 conversion rounds a float32 to the nearest E2M1
+  // level with ties to the even encoding and saturates at 6 -- the same
+  // rule as exact() -- but keeps the sign of a zero result (code 8).
+  // Element 2p goes to nibble 2p of the word, 2p + 1 to nibble 2p + 1.
+  __device__ static __forceinline__ uint32_t cvt8(const float* y) {
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+    return w;
+  }
+  // Codes of N estimates (|y - x| below 2^-21 |x|): every value in
+  // [y (1 - 2^-20), y (1 + 2^-20)] contains x, and rounding is monotone, so
+  // when both ends give the same codes those are the codes of x. Otherwise
+  // returns true and the caller re-decides with exact(). A zero code may
+  // come back as -0, which is arithmetically harmless.
+  template <int N>
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q) {
+    static_assert(N % 8 == 0, "groups of 8");
+    uint32_t diff = 0u;
+#pragma unroll
+    for (int g = 0; g < N; g += 8) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float yc = __builtin_amdgcn_fmed3f(y[g + k], -8.0f, 8.0f);
+        lo[k] = yc * (1.0f - 0x1p-20f);
+        hi[k] = yc * (1.0f + 0x1p-20f);
+      }
+      const uint32_t wl = cvt8(lo), wh = cvt8(hi);
+      diff |= wl ^ wh;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 r;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 0); q[g + 0] = r.x; q[g + 1] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 1); q[g + 2] = r.x; q[g + 3] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 2); q[g + 4] = r.x; q[g + 5] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 3); q[g + 6] = r.x; q[g + 7] = r.y;
+    }
+    return diff != 0u;
+  }
+  // Nibbles of 8 codes (exact E2M1 values, so the conversion is exact);
+  // a zero is stored as +0.
+  __device__ static __forceinline__ uint32_t pack8(const float* q) {
+    const uint32_t w = cvt8(q);
+    const uint32_t mag = w & 0x77777777u;
+    const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;  // bit 3 set iff magnitude != 0
+    return w & (0x77777777u | nonzero);
   }
 };
 

@@ -276,7 +276,6 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       // near a rounding midpoint the sums are redone with exact codes.
       double num[NB], den[NB];
       float q[LC];  // Q1 here; becomes Q2 below
-      float flag = 0.0f;
       // The sums of a block run in DQ_ROW_CHAINS interleaved partial sums
       // (more independent float64 chains in flight), combined pairwise.
       auto row_sums = [&]() {
@@ -304,17 +303,14 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         }
       };
       {
-        float ra[NB];
+        float ra[NB], y[LC];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) ra[bl] = __builtin_amdgcn_rcpf(a_old[bl]);
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-          for (int k = 0; k < BL; ++k) {
-            const int e = bl * BL + k;
-            q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra[bl], flag);
-          }
-        if (wave_any(flag > kTieFlag)) {
+          for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra[bl];
+        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q))) {
 #pragma unroll
           for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -350,17 +346,14 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) changed |= a_new[bl] != a_old[bl];
       if (wave_any(changed)) {
-        flag = 0.0f;
+        float y[LC];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
           const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
 #pragma unroll
-          for (int k = 0; k < BL; ++k) {
-            const int e = bl * BL + k;
-            q[e] = Grid<GRID>::fast(w[e] * LRB(e) * ra, flag);
-          }
+          for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra;
         }
-        if (wave_any(flag > kTieFlag)) {
+        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q))) {
 #pragma unroll
           for (int bl = 0; bl < NB; ++bl) {
             const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
@@ -440,36 +433,74 @@ static __global__ void __launch_bounds__(kTileCols)
 
 // ------------------------------------------------------------------ pack
 
-// One thread per (row, 16 columns): exact codes, 8 bytes out.
+// One thread per (16 columns, kPackRows rows), 8 bytes out per row; the
+// column reciprocals are formed once per thread. Codes come from the float32
+// estimate of W/(a b) (reciprocals: relative error below 4 units of 2^-24);
+// a wave with any element near a rounding midpoint re-decides that row's
+// codes exactly, as the pass kernel does.
+constexpr int kPackRows = 4;
+
 template <int WT, int GRID, int AFMT, int G>
 __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, int64_t ldw,
                                                    int64_t M, int64_t N, const void* __restrict__ a_,
                                                    const uint16_t* __restrict__ b,
                                                    uint8_t* __restrict__ packed) {
   using AT = typename ScaleStore<AFMT>::T;
+  constexpr int BL = G < 16 ? G : 16;  // elements of one block in this thread
+  constexpr int NB = 16 / BL;
   const int64_t nch = N / 16;
+  const int64_t n_rg = (M + kPackRows - 1) / kPackRows;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= M * nch) return;
-  const int64_t row = idx / nch, col = (idx - row * nch) * 16;
-  const float av = decode_scale<AFMT>(reinterpret_cast<const AT*>(a_)[row * (N / G) + col / G]);
-  const float ra = 1.0f / av;
-  float w[16];
-  load8<WT>(W, row * ldw + col, w);
-  load8<WT>(W, row * ldw + col + 8, w + 8);
-  uint32_t word[2] = {0u, 0u};
+  const bool live = idx < n_rg * nch;
+  const int64_t cidx = live ? idx : 0;  // dead lanes compute on element 0
+  const int64_t rg = cidx / nch, col = (cidx - rg * nch) * 16;
+  const uint4 bv0 = *reinterpret_cast<const uint4*>(b + col);
+  const uint4 bv1 = *reinterpret_cast<const uint4*>(b + col + 8);
+  const uint32_t bw[8] = {bv0.x, bv0.y, bv0.z, bv0.w, bv1.x, bv1.y, bv1.z, bv1.w};
+  float bj[16], rb[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const float bj = fp16_bits_to_float(b[col + k]);
-    const float q = Grid<GRID>::exact(w[k] * (1.0f / bj) * ra, w[k], av, bj);
-    word[k >> 3] |= Grid<GRID>::nibble(q) << (4 * (k & 7));
+    bj[k] = fp16_bits_to_float((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));
+    rb[k] = __builtin_amdgcn_rcpf(bj[k]);
   }
-  *reinterpret_cast<uint2*>(packed + row * (N / 2) + col / 2) = make_uint2(word[0], word[1]);
+#pragma unroll
+  for (int r = 0; r < kPackRows; ++r) {
+    const int64_t row_raw = rg * kPackRows + r;
+    const bool ok = live && row_raw < M;
+    const int64_t row = ok ? row_raw : 0;
+    RawRow<WT, 16> raw;
+    raw.load(W, row * ldw + col);
+    float av[NB];
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl)
+      av[bl] = decode_scale<AFMT>(reinterpret_cast<const AT*>(a_)[row * (N / G) + (col + bl * BL) / G]);
+    float w[16], y[16], q[16];
+    raw.unpack(w);
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) {
+      const float ra = __builtin_amdgcn_rcpf(av[bl]);
+#pragma unroll
+      for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
+    }
+    if (wave_any(Grid<GRID>::template fast_n<16>(y, q))) {
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+        for (int k = bl * BL; k < (bl + 1) * BL; ++k)
+          q[k] = Grid<GRID>::exact(w[k] / (av[bl] * bj[k]), w[k], av[bl], bj[k]);
+    }
+    const uint2 word = make_uint2(Grid<GRID>::pack8(q), Grid<GRID>::pack8(q + 8));
+    if (ok) *reinterpret_cast<uint2*>(packed + row * (N / 2) + col / 2) = word;
+  }
 }
 
 // ------------------------------------------------------- activation side
 
-// One thread per (token, block): X' = X D_b (exact in float32 for bf16 X),
-// s = Pi(absmax / qmax), codes = q(X' / s).
+// One lane per 8 consecutive channels of a token (one 16-byte load of X and
+// of b), G/8 lanes per block: X' = X D_b (exact in float32 for bf16 X),
+// block absmax by lane shuffles, s = Pi(absmax / qmax), codes from the
+// float32 estimate X' * (1/s) with the exact re-decision of a wave that has
+// an element near a rounding midpoint.
 template <int GRID, int AFMT, int G>
 __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                         int64_t T, int64_t N,
@@ -477,37 +508,39 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
                                                         uint8_t* __restrict__ xq,
                                                         void* __restrict__ xs_) {
   using AT = typename ScaleStore<AFMT>::T;
-  const int64_t nblk = N / G;
+  constexpr int LPB = G / 8;  // lanes per block; a block never straddles a wave
+  const int64_t nch = N / 8;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * nblk) return;
-  const int64_t t = idx / nblk, col = (idx - t * nblk) * G;
-  float x[G];
+  const bool live = idx < T * nch;
+  const int64_t cidx = live ? idx : 0;  // dead lanes compute on chunk 0
+  const int64_t t = cidx / nch, col = (cidx - t * nch) * 8;
+  const uint4 xv = *reinterpret_cast<const uint4*>(X + t * ldx + col);
+  const uint4 bv = *reinterpret_cast<const uint4*>(b + col);
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  float x[8];
   float amax = 0.0f;
 #pragma unroll
-  for (int c = 0; c < G / 8; ++c) {
-    load8<kWBF16>(X, t * ldx + col + 8 * c, &x[8 * c]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      x[8 * c + k] *= fp16_bits_to_float(b[col + 8 * c + k]);  // exact product
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(x[8 * c + k]));
-    }
+  for (int k = 0; k < 8; ++k) {
+    const float xk = (k & 1) ? bf16_hi(xw[k >> 1]) : bf16_lo(xw[k >> 1]);
+    x[k] = xk * fp16_bits_to_float((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));  // exact product
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
   }
+#pragma unroll
+  for (int m = 1; m < LPB; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m));
   const double s = amax > 0.0f ? project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0;
-  const float sf = (float)s, rs = 1.0f / sf;
-  uint32_t word[G / 8];
+  const float sf = (float)s, rs = __builtin_amdgcn_rcpf(sf);
+  float y[8], q[8];
 #pragma unroll
-  for (int c = 0; c < G / 8; ++c) {
-    word[c] = 0u;
+  for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
+  if (wave_any(Grid<GRID>::template fast_n<8>(y, q))) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float q = Grid<GRID>::exact(x[8 * c + k] * rs, x[8 * c + k], sf, 1.0f);
-      word[c] |= Grid<GRID>::nibble(q) << (4 * k);
-    }
+    for (int k = 0; k < 8; ++k) q[k] = Grid<GRID>::exact(x[k] / sf, x[k], sf, 1.0f);
   }
-  uint8_t* dst = xq + t * (N / 2) + col / 2;
-#pragma unroll
-  for (int c = 0; c < G / 8; ++c) reinterpret_cast<uint32_t*>(dst)[c] = word[c];
-  reinterpret_cast<AT*>(xs_)[idx] = encode_scale<AFMT>(s);
+  const uint32_t word = Grid<GRID>::pack8(q);
+  if (live) {
+    reinterpret_cast<uint32_t*>(xq + t * (N / 2))[col / 8] = word;
+    if ((threadIdx.x % LPB) == 0) reinterpret_cast<AT*>(xs_)[t * (N / G) + col / G] = encode_scale<AFMT>(s);
+  }
 }
 
 // ------------------------------------------------------------- launchers
@@ -547,15 +580,16 @@ hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, con
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
                        const uint16_t* b, uint8_t* packed, hipStream_t st) {
-  pack_kernel<WT, GRID, AFMT, G><<<blocks_for(M * (N / 16), 256), 256, 0, st>>>(W, ldw, M, N, a, b,
-                                                                              packed);
+  const int64_t n_rg = (M + kPackRows - 1) / kPackRows;
+  pack_kernel<WT, GRID, AFMT, G><<<blocks_for(n_rg * (N / 16), 256), 256, 0, st>>>(W, ldw, M, N, a, b,
+                                                                                packed);
   return hipGetLastError();
 }
 
 template <int GRID, int AFMT, int G>
 hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, const uint16_t* b,
                       uint8_t* xq, void* xs, hipStream_t st) {
-  act_quant_kernel<GRID, AFMT, G><<<blocks_for(T * (N / G), 256), 256, 0, st>>>(X, ldx, T, N, b, xq,
+  act_quant_kernel<GRID, AFMT, G><<<blocks_for(T * (N / 8), 256), 256, 0, st>>>(X, ldx, T, N, b, xq,
                                                                               xs);
   return hipGetLastError();
 }

@@ -3,7 +3,8 @@
 Runs, each in its own rocprofv3 process:
   1. --kernel-trace --stats of ``bench.py`` (per-kernel average durations);
   2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of ``bench.py`` (HBM bytes per
-     dispatch, in KiB);
+     dispatch, in KiB), then --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_WAVES
+     (instructions issued by the pass kernel);
   3. the same two counters for ``bench.py --copy-calibration``, a plain
      device copy of 256 MiB, whose known bytes give the scale factors of
      the two counters.
@@ -121,6 +122,15 @@ def main():
         res[("copy", counter)] = vals
         cmds[("copy", counter)] = c
 
+    # 4. VALU instruction count of the pass kernel (wave-level instructions;
+    #    x64 lanes = lane operations), for its VALU roofline
+    d, c = _rocprof(["--pmc", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAVES"],
+                    bench_args + ["--steps", "2", "--warmup", "1"], "pass_valu", work, timeout=180)
+    valu = _counters(d, "SQ_INSTS_VALU", "bcd_pass_kernel")
+    salu = _counters(d, "SQ_INSTS_SALU", "bcd_pass_kernel")
+    waves = _counters(d, "SQ_WAVES", "bcd_pass_kernel")
+    cmds[("pass", "VALU")] = c
+
     copy_bytes = 256 << 20
     # the copy kernel is the largest dispatch of the calibration run
     f_copy = max(res[("copy", "FETCH_SIZE")]) * 1024.0
@@ -151,6 +161,10 @@ def main():
         "write_factor": write_factor,
         "traffic_bytes_per_launch": traffic,
         "traffic_bytes_per_element": traffic / (M * N),
+        "valu_insts_per_launch": sum(valu) / len(valu),
+        "salu_insts_per_launch": sum(salu) / len(salu),
+        "waves_per_launch": sum(waves) / len(waves),
+        "valu_lane_ops_per_element": 64.0 * sum(valu) / len(valu) / (M * N),
         "commands": {f"{k[0]}_{k[1]}": v for k, v in cmds.items()},
     }
     json.dump(rec, open(os.path.join(args.out_dir, "bcd_pass_counters.json"), "w"), indent=2)
@@ -162,6 +176,9 @@ def main():
           f"{write_factor:.4f} (write).", "",
           f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per weight "
           f"element (algorithmic: {b_alg:.4f}).", "",
+          f"VALU: {rec['valu_insts_per_launch']:.4g} wave instructions per launch "
+          f"({rec['valu_lane_ops_per_element']:.2f} lane operations per weight element), "
+          f"SALU {rec['salu_insts_per_launch']:.4g}, waves {rec['waves_per_launch']:.0f}.", "",
           "Commands:", ""]
     md += [f"    {v}" for v in cmds.values()]
     open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.md"), "w").write("\n".join(md) + "\n")

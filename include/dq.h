@@ -114,8 +114,9 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
                    double* stats, void* stream);
 
 /* Final codes Q = q(W/(a b)), packed two per byte (summary App. I: packed
- * offline for deployment). cols must be even.
- *   packed  out  [rows, cols/2] uint8, row pitch cols/2 */
+ * offline for deployment).
+ *   b       in   [cols] fp16 bits, 16-byte aligned
+ *   packed  out  [rows, cols/2] uint8, row pitch cols/2, 8-byte aligned */
 int dq_pack_codes(const dq_problem* p, const void* W, const void* a,
                   const uint16_t* b, uint8_t* packed, void* stream);
 
@@ -125,10 +126,11 @@ int dq_pack_codes(const dq_problem* p, const void* W, const void* a,
  * quantization; reproduction README "Core equations"). For every token t
  * and block g of G channels: X' = X D_b, s = Pi_Fa(absmax(X'_tg) / qmax)
  * (1 if zero), codes = q(X'_tg / s).
- *   X         in   [tokens, ldx] of p->w_type; p->cols channels are used
+ *   X         in   [tokens, ldx] of p->w_type (bf16 only); p->cols channels
+ *                  are used; base and row pitch 16-byte aligned
  *   tokens    number of rows of X (>= 0; 0 is a no-op)
- *   b         in   [cols] fp16 bits
- *   xq        out  [tokens, cols/2] packed codes
+ *   b         in   [cols] fp16 bits, 16-byte aligned
+ *   xq        out  [tokens, cols/2] packed codes, 16-byte aligned
  *   x_scales  out  [tokens, cols/G] in a_fmt's encoding */
 int dq_rescale_quantize_act(const dq_problem* p, const void* X, int64_t tokens,
                             int64_t ldx, const uint16_t* b, uint8_t* xq,

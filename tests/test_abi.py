@@ -91,6 +91,7 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert L.dq_init_rtn(None, ok, ok, ok, None) == dq.ERR_INVALID_ARG
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, -1, ok, 1 << 20, None, None) == dq.ERR_INVALID_ARG
     assert L.dq_pack_codes(ctypes.byref(p), ok, ok, ok, ctypes.c_void_p(259), None) == dq.ERR_INVALID_ARG
+    assert L.dq_pack_codes(ctypes.byref(p), ok, ok, ctypes.c_void_p(258), ok, None) == dq.ERR_INVALID_ARG
 
 
 def test_iterate_checks_workspace_and_stats_before_launch():

@@ -93,6 +93,50 @@ def test_exact_ties_power_of_two_scales():
     _check(data, fmt, 3, "mxint4 ties iterated")
 
 
+def test_exact_ties_e2m1_power_of_two_scales():
+    # The same for the E2M1 grid: with E8M0 block scales and b = 1, bf16
+    # weights land exactly on the E2M1 midpoints (0.25, 0.75, ..., 5) often;
+    # ties go to the even encoding on both sides.
+    data = _mat(256, 256, 9, n_out=0)
+    fmt = NAMED["mxfp4_g32"]
+    g = GpuRun(data, fmt).run(0)
+    W64 = as_f64(data)
+    sol = D.solve(W64, oracle_fmt(fmt), 0)
+    ties = D.code_ties(W64, sol.a, sol.b, oracle_fmt(fmt))
+    assert ties.sum() > 100
+    np.testing.assert_array_equal(g.Q, sol.Q)
+    np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, oracle_fmt(fmt)))
+    _check(data, fmt, 3, "mxfp4 ties iterated")
+
+
+def test_activation_e2m1_midpoints_and_neighbours():
+    # Blocks whose absmax is 6 get the E8M0 scale 1 with b = 1, so the codes
+    # are the E2M1 rounding of the values themselves: every midpoint, its
+    # bf16 neighbours on both sides, and both signs.
+    fmt = NAMED["mxfp4_g32"]
+    ofmt = oracle_fmt(fmt)
+    mb = synth.bf16_bits(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]))
+    pos = np.concatenate([mb, mb - 1, mb + 1,                   # bf16 neighbours of each midpoint
+                          synth.bf16_bits(np.array([0.0, 0.1, 5.9, 6.0, 0.5, 3.0]))])
+    bits = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)  # both signs
+    N = 32
+    tokens = (len(bits) + N - 2) // (N - 1)
+    X = np.zeros((tokens, N), dtype=np.uint16)
+    flat = np.zeros(tokens * (N - 1), dtype=np.uint16)
+    flat[:len(bits)] = bits
+    X[:, :N - 1] = flat.reshape(tokens, N - 1)
+    X[:, N - 1] = synth.bf16_bits(np.array([6.0]))[0]          # absmax 6 -> scale 1
+    b = torch.full((N,), 0x3C00, dtype=torch.int16, device="cuda")
+    p = dq.problem(tokens, N, fmt, dq.W_BF16, N)
+    xq = torch.empty((tokens, N // 2), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((tokens, N // fmt.group), dtype=fmt.a_dtype, device="cuda")
+    dq.rescale_quantize_act(p, torch.from_numpy(X.view(np.int16)).cuda(), tokens, N, b, xq, xs)
+    torch.cuda.synchronize()
+    codes, scales = D.rescale_quantize_act(synth.bf16_to_f64(X), np.ones(N), ofmt)
+    assert np.all(scales == 1.0)
+    np.testing.assert_array_equal(xq.cpu().numpy(), D.pack_codes(codes, ofmt))
+
+
 def test_zero_slices():
     data = _mat(128, 256, 4)
     data[5, 64:128] = 0                # an all-zero block (bf16 zero bits)
