@@ -183,13 +183,18 @@ template <> struct Grid<kGridInt4> {
     return (uint32_t)((int)q) & 0xFu;
   }
   // Codes of N estimates; true if any of them may round differently at the
-  // exact quotient (then the caller re-decides with exact()).
+  // exact quotient (then the caller re-decides those with exact(); near()
+  // tells which). diff is unused here.
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
     float flag = 0.0f;
 #pragma unroll
     for (int e = 0; e < N; ++e) q[e] = fast(y[e], flag);
     return flag > kTieFlag;
+  }
+  __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
+                                              int e) {
+    return __builtin_fabsf(__builtin_amdgcn_fmed3f(y[e], -8.25f, 7.25f) - q[e]) > kTieFlag;
   }
   // Nibbles of 8 codes, element k in bits 4k..4k+3.
   __device__ static __forceinline__ uint32_t pack8(const float* q) {
@@ -251,10 +256,11 @@ template <> struct Grid<kGridE2M1> {
   // when both ends give the same codes those are the codes of x. Otherwise
   // returns true and the caller re-decides with exact(). A zero code may
   // come back as -0, which is arithmetically harmless.
+  // diff[g] receives the differing nibbles of group g (near() reads them).
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
     static_assert(N % 8 == 0, "groups of 8");
-    uint32_t diff = 0u;
+    uint32_t any = 0u;
 #pragma unroll
     for (int g = 0; g < N; g += 8) {
       float lo[8], hi[8];
@@ -265,7 +271,8 @@ template <> struct Grid<kGridE2M1> {
         hi[k] = yc * (1.0f + 0x1p-20f);
       }
       const uint32_t wl = cvt8(lo), wh = cvt8(hi);
-      diff |= wl ^ wh;
+      diff[g / 8] = wl ^ wh;
+      any |= wl ^ wh;
       typedef float f2 __attribute__((ext_vector_type(2)));
       f2 r;
       r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 0); q[g + 0] = r.x; q[g + 1] = r.y;
@@ -273,7 +280,11 @@ template <> struct Grid<kGridE2M1> {
       r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 2); q[g + 4] = r.x; q[g + 5] = r.y;
       r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 3); q[g + 6] = r.x; q[g + 7] = r.y;
     }
-    return diff != 0u;
+    return any != 0u;
+  }
+  __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
+                                              int e) {
+    return ((diff[e >> 3] >> (4 * (e & 7))) & 0xFu) != 0u;
   }
   // Nibbles of 8 codes (exact E2M1 values, so the conversion is exact);
   // a zero is stored as +0.

@@ -310,13 +310,16 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra[bl];
-        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q))) {
+        uint32_t diff[LC / 8];
+        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
+          // only the element slots where some lane is near a midpoint
 #pragma unroll
           for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
             for (int k = 0; k < BL; ++k) {
               const int e = bl * BL + k;
-              q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra[bl], w[e], a_old[bl], LB(e));
+              if (wave_any(Grid<GRID>::near(y, q, diff, e)))
+                q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], LB(e));
             }
         }
         row_sums();
@@ -353,16 +356,16 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra;
         }
-        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q))) {
+        uint32_t diff[LC / 8];
+        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
 #pragma unroll
-          for (int bl = 0; bl < NB; ++bl) {
-            const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
+          for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
             for (int k = 0; k < BL; ++k) {
               const int e = bl * BL + k;
-              q[e] = Grid<GRID>::exact(w[e] * LRB(e) * ra, w[e], a_new[bl], LB(e));
+              if (wave_any(Grid<GRID>::near(y, q, diff, e)))
+                q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], LB(e));
             }
-          }
         }
       }
 
@@ -482,12 +485,14 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
 #pragma unroll
       for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
     }
-    if (wave_any(Grid<GRID>::template fast_n<16>(y, q))) {
+    uint32_t diff[2];
+    if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff))) {
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
         for (int k = bl * BL; k < (bl + 1) * BL; ++k)
-          q[k] = Grid<GRID>::exact(w[k] / (av[bl] * bj[k]), w[k], av[bl], bj[k]);
+          if (wave_any(Grid<GRID>::near(y, q, diff, k)))
+            q[k] = Grid<GRID>::exact(y[k], w[k], av[bl], bj[k]);
     }
     const uint2 word = make_uint2(Grid<GRID>::pack8(q), Grid<GRID>::pack8(q + 8));
     if (ok) *reinterpret_cast<uint2*>(packed + row * (N / 2) + col / 2) = word;
@@ -532,9 +537,11 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
   float y[8], q[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
-  if (wave_any(Grid<GRID>::template fast_n<8>(y, q))) {
+  uint32_t diff[1];
+  if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = Grid<GRID>::exact(x[k] / sf, x[k], sf, 1.0f);
+    for (int k = 0; k < 8; ++k)
+      if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
   }
   const uint32_t word = Grid<GRID>::pack8(q);
   if (live) {
