@@ -96,6 +96,24 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def recorded_valu(workload: str):
+    """VALU lane operations per pass launch from the committed rocprofv3
+    SQ_INSTS_VALU measurement (wave instructions x 64), or None."""
+    try:
+        rec = json.load(open(COUNTERS_JSON))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    v = rec.get("valu_insts_per_launch")
+    return None if v is None else 64.0 * v
+
+
+#: Non-packed VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+#: (one wave64 instruction per SIMD every 4 cycles).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
 def copy_calibration(nbytes: int = 256 << 20, reps: int = 3):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of the profiled kernels."""
@@ -117,26 +135,33 @@ def _make_set_matrix(item):
     return l, p, synth.make_matrix(spec, seed).data
 
 
-def set_cpu_baseline(items, budget_s: float = 20.0):
-    """The float64 oracle on a bounded sample of the set: the first column
-    stripes of layer 0's matrices, as many as fit the budget."""
+def set_cpu_baseline(items, budget_s: float = 15.0):
+    """The float64 oracle on a bounded sample of the set: the leading column
+    stripes of each of layer 0's seven matrices, as many per matrix as fit
+    the budget (sized from a first run on two stripes each)."""
     from oracle import dualquant as D
     from calibration_free_bit_amd import synth
     fmt = D.FORMATS["int4_g64"]
-    done, elems, t_used, parts = 0, 0, 0.0, []
-    for (l, p, name, spec, seed) in items[:7]:
-        if t_used > budget_s:
-            break
-        data = synth.make_matrix(spec, seed).data
-        W = synth.bf16_to_f64(data[:, :2 * fmt.group])
+    G = fmt.group
+    layer0 = [(name, synth.bf16_to_f64(synth.make_matrix(spec, seed).data))
+              for (l, p, name, spec, seed) in items[:7]]
+
+    def run(k):
         t0 = time.perf_counter()
-        D.solve(W, fmt, 20)
-        t_used += time.perf_counter() - t0
-        elems += W.size
-        parts.append(f"{name} {W.shape[0]}x{W.shape[1]}")
-    return {"value": elems * 20 / t_used, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": "float64 numpy oracle, first 2 column stripes of layer 0's " + ", ".join(parts)
-                      + f"; T=20, {t_used:.1f} s"}
+        n = 0
+        for name, W in layer0:
+            Ws = W[:, :k * G]
+            D.solve(Ws, fmt, 20)
+            n += Ws.size
+        return n, time.perf_counter() - t0
+
+    n, dt = run(2)
+    k = max(2, min(min(W.shape[1] for _, W in layer0) // G, int(2 * budget_s / max(dt, 1e-3))))
+    n, dt = run(k)
+    return {"value": n * 20 / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle, the first {k} column stripes (G={G}) of each of layer 0's "
+                      f"seven matrices ({', '.join(f'{nm} {W.shape[0]}x{k * G}' for nm, W in layer0)}); "
+                      f"T=20, {dt:.1f} s"}
 
 
 def run_set(args):
@@ -300,6 +325,7 @@ def main():
                      "traffic": recorded_traffic(wl.name),
                      "kernel": "bcd_pass_kernel", "alg_bytes_per_elem": b_alg,
                      "avg_launch_us": pass_s * 1e6},
+        "valu": valu_entry(recorded_valu(wl.name), pass_s, elems),
         "breakdown_ms": {"init": init_ms, "iterate": iter_ms, "pack": pack_ms,
                          "wall_per_step": wall * 1e3 / args.steps},
         "iterate_elements_per_s_per_iter": elems / pass_s,
@@ -307,6 +333,16 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data)
     print(json.dumps(out))
+
+
+def valu_entry(lane_ops, pass_s: float, elems: int):
+    """The pass kernel against the VALU issue peak, the unit that binds it:
+    recorded lane operations per launch over the launch time measured here."""
+    if lane_ops is None:
+        return None
+    achieved = lane_ops / pass_s / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS, "unit": "T lane-op/s",
+            "frac": achieved / VALU_PEAK_TOPS, "lane_ops_per_elem": lane_ops / elems}
 
 
 def fmt_w_bf16(data) -> bool:

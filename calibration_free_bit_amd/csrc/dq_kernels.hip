@@ -275,7 +275,8 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       // least-squares sums (R = Q1 D_b). If any element of the wave lies
       // near a rounding midpoint the sums are redone with exact codes.
       double num[NB], den[NB];
-      float q[LC];  // Q1 here; becomes Q2 below
+      float q[LC];    // Q1 here; becomes Q2 below
+      float wrb[LC];  // W / b (rounded), shared by both requantizations
       // The sums of a block run in DQ_ROW_CHAINS interleaved partial sums
       // (more independent float64 chains in flight), combined pairwise.
       auto row_sums = [&]() {
@@ -307,9 +308,11 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) ra[bl] = __builtin_amdgcn_rcpf(a_old[bl]);
 #pragma unroll
+        for (int e = 0; e < LC; ++e) wrb[e] = w[e] * LRB(e);
+#pragma unroll
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-          for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra[bl];
+          for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
         uint32_t diff[LC / 8];
         if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
           // only the element slots where some lane is near a midpoint
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         for (int bl = 0; bl < NB; ++bl) {
           const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
 #pragma unroll
-          for (int k = 0; k < BL; ++k) y[bl * BL + k] = w[bl * BL + k] * LRB(bl * BL + k) * ra;
+          for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra;
         }
         uint32_t diff[LC / 8];
         if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
