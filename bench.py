@@ -239,7 +239,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
-    ap.add_argument("--streams", type=int, default=4, help="streams of the Llama set workload")
+    ap.add_argument("--streams", type=int, default=2, help="streams of the Llama set workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (for scaling byte counters)")
