@@ -129,6 +129,26 @@ def init_rtn(W, fmt: Format):
     return a, b
 
 
+def init_colnorm(W, fmt: Format):
+    """Initialization from per-column L1 norms and format-native row absmax.
+
+    [DQ summary] §5.3: the starting point combines format-native row absmax
+    scales with per-column L1-norm scales; the page gives no formula.
+    Reading (listed in the design doc): the column inverse scale is its column's
+    mean absolute value projected onto F_b, b_j = Pi_Fb(sum_i |W_ij| / M)
+    (1 for an all-zero column), and the block scales are the absmax
+    initialization applied to W D_b^-1,
+    a_ig = Pi_Fa(max_{j in g} |W_ij / b_j| / qmax) (1 for a zero block).
+    Returns (a [M, N/G], b [N]).
+    """
+    W = _check(W, fmt)
+    M = W.shape[0]
+    colmean = np.abs(W).sum(axis=0) / M
+    b = np.where(colmean > 0, F.project(np.where(colmean > 0, colmean, 1.0), fmt.b_fmt), 1.0)
+    a, _ = init_rtn(W / b[None, :], fmt)
+    return a, b
+
+
 def update_a(W, Q, b, fmt: Format) -> np.ndarray:
     """Closed-form row/block update with the codes and b fixed.
 

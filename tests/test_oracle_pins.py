@@ -409,3 +409,56 @@ def test_activation_rescale_follows_the_factorization(fmt):
     assert np.all(np.abs(Xb - rec)[ok] <= half[ok] * (1 + 1e-12))
     # and the scales are legal and positive
     np.testing.assert_array_equal(F.project(xs, fmt.a_fmt), xs)
+
+
+# ------------------------------- column-norm initializer ([DQ summary] §5.3)
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colnorm_init_rank_one_closed_form(fmt):
+    # W_ij = s_i * t_j with s_i = +-1 and t_j powers of two: every column's
+    # mean |W| is t_j itself (legal in fp16), so b = t exactly, W / b = s and
+    # every block scale is the projection of 1 / qmax.
+    rng = np.random.default_rng(3)
+    M, N = 16, 4 * fmt.group
+    s = rng.choice([-1.0, 1.0], M)
+    t = 2.0 ** rng.integers(-8, 4, N)
+    a, b = D.init_colnorm(np.outer(s, t), fmt)
+    np.testing.assert_array_equal(b, t)
+    np.testing.assert_array_equal(a, np.full((M, N // fmt.group), F.project(1.0 / fmt.qmax, fmt.a_fmt)))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colnorm_init_zero_slices_and_column_equivariance(fmt):
+    W = _w(32, 4 * fmt.group, 5)
+    W[:, 7] = 0.0                       # all-zero column -> b = 1
+    W[3, :fmt.group] = 0.0              # all-zero block -> a = 1
+    a, b = D.init_colnorm(W, fmt)
+    assert b[7] == 1.0 and a[3, 0] == 1.0
+    assert np.all(a > 0) and np.all(b > 0)
+    np.testing.assert_array_equal(F.project(b, "fp16"), b)
+    np.testing.assert_array_equal(F.project(a.ravel(), fmt.a_fmt), a.ravel())
+    # scaling one column by 2^k scales its b by 2^k and leaves a unchanged
+    W2 = W.copy()
+    W2[:, 11] *= 8.0
+    a2, b2 = D.init_colnorm(W2, fmt)
+    assert b2[11] == 8.0 * b[11]
+    np.testing.assert_array_equal(np.delete(b2, 11), np.delete(b, 11))
+    np.testing.assert_array_equal(a2, a)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_colnorm_init_equals_exact_rational_definition(fmt):
+    # the definition re-done in exact rational arithmetic on a small matrix
+    f = _small_fmt(fmt, 16)
+    W = _w(6, 32, 17)
+    a, b = D.init_colnorm(W, f)
+    Wf = [[Fraction(float(x)) for x in row] for row in W]
+    M, N = len(Wf), len(Wf[0])
+    for j in range(N):
+        m = sum(abs(Wf[i][j]) for i in range(M)) / M
+        assert Fraction(float(b[j])) == (_frac_project(m, "fp16") if m > 0 else 1)
+    for i in range(M):
+        for g in range(N // 16):
+            amax = max(abs(Wf[i][j]) / Fraction(float(b[j])) for j in range(g * 16, g * 16 + 16))
+            want = _frac_project(amax / Fraction(int(f.qmax)), f.a_fmt) if amax > 0 else 1
+            assert Fraction(float(a[i, g])) == want, (i, g)

@@ -136,3 +136,31 @@ def test_column_sums_over_wrong_axis_is_caught(monkeypatch, axis_bug):
     monkeypatch.setattr(D, "update_b", bad)
     assert _fails((TP.test_column_stripes_decouple, {"fmt": D.INT4_G64}),
                   (TP.test_column_update_is_brute_force_argmin, {"fmt": D.INT4_G64, "seed": 0}))
+
+
+def _colnorm_pins():
+    return [(TP.test_colnorm_init_rank_one_closed_form, {"fmt": f}) for f in TP.FMTS] + \
+           [(TP.test_colnorm_init_equals_exact_rational_definition, {"fmt": f}) for f in TP.FMTS] + \
+           [(TP.test_colnorm_init_zero_slices_and_column_equivariance, {"fmt": f}) for f in TP.FMTS]
+
+
+def test_colnorm_max_instead_of_mean_is_caught(monkeypatch):
+    def bad(W, fmt):
+        W = np.asarray(W, dtype=np.float64)
+        cm = np.abs(W).max(axis=0)
+        b = np.where(cm > 0, F.project(np.where(cm > 0, cm, 1.0), fmt.b_fmt), 1.0)
+        a, _ = D.init_rtn(W / b[None, :], fmt)
+        return a, b
+    monkeypatch.setattr(D, "init_colnorm", bad)
+    assert _fails(*_colnorm_pins())
+
+
+def test_colnorm_block_scales_without_column_division_are_caught(monkeypatch):
+    orig = D.init_colnorm
+
+    def bad(W, fmt):
+        _, b = orig(W, fmt)
+        a, _ = D.init_rtn(W, fmt)
+        return a, b
+    monkeypatch.setattr(D, "init_colnorm", bad)
+    assert _fails(*_colnorm_pins())
