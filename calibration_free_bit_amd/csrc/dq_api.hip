@@ -61,8 +61,12 @@ Workspace pass_geometry(const dq_problem* p) {
     const int64_t first = (t * g.S) / g.L, last = ((t + 1) * g.S - 1) / g.L;
     g.max_seg = std::max(g.max_seg, last - first + 1);
   }
-  // two alternating buffers of [n_tiles][max_seg][64][2] float64 partials
-  w.bytes = align256(2 * size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double));
+  // two alternating buffers of [n_tiles][max_seg][64][2] float64 partials;
+  // the column-norm initialization uses [n_tiles][chunks][64] float64
+  const size_t pass_bytes = 2 * size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double);
+  const size_t init_bytes = size_t(g.n_tiles) * size_t(ceil_div(p->rows, dq::kColnormRows)) *
+                            dq::kTileCols * sizeof(double);
+  w.bytes = align256(std::max(pass_bytes, init_bytes));
   return w;
 }
 
@@ -130,6 +134,20 @@ int dq_init_rtn(const dq_problem* p, const void* W, void* a, uint16_t* b, void* 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
     return hip_status(dq::launch_init<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, st));
+  });
+}
+
+int dq_init_colnorm(const dq_problem* p, const void* W, void* a, uint16_t* b, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (!W || !a || !b || !aligned16(W)) return DQ_ERR_INVALID_ARG;
+  const Workspace ws = pass_geometry(p);
+  if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DQ_ERR_WORKSPACE;
+  double* part = static_cast<double*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_init_colnorm<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, part, st));
   });
 }
 

@@ -31,6 +31,14 @@ struct PassGeom {
 // Workspace: two alternating [n_tiles][max_seg][64][2] float64 buffers of
 // column partial sums.
 
+// Rows per chunk of the column-norm initialization's partial sums; its
+// workspace holds [n_tiles][ceil(M / kColnormRows)][64] float64.
+constexpr int kColnormRows = 256;
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
+                               double* part, hipStream_t st);
+
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                        hipStream_t st);

@@ -71,6 +71,77 @@ __global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ 
   if (idx < N) b[idx] = 0x3C00u;  // fp16 1.0
 }
 
+// ------------------------------------------- column-norm initialization
+
+// Partial column sums of |W| over chunks of kColnormRows rows: a workgroup
+// of 64 columns x 4 row-lanes per (tile, chunk); each lane adds every 4th
+// row of the chunk in order, then the 4 row-lanes are added pairwise.
+template <int WT>
+__global__ void __launch_bounds__(256) colnorm_partial_kernel(const void* __restrict__ W, int64_t ldw,
+                                                              int64_t M, int64_t N,
+                                                              double* __restrict__ part) {
+  __shared__ double s_sum[4][kTileCols];
+  const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  const int64_t tile = blockIdx.x, chunk = blockIdx.y;
+  const int64_t j = tile * kTileCols + c;
+  const int64_t r0 = chunk * kColnormRows, r1 = min(r0 + kColnormRows, M);
+  double acc = 0.0;
+  if (j < N) {
+    for (int64_t r = r0 + rl; r < r1; r += 4) {
+      float v;
+      if constexpr (WT == kWBF16)
+        v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[r * ldw + j] << 16);
+      else
+        v = reinterpret_cast<const float*>(W)[r * ldw + j];
+      acc += (double)__builtin_fabsf(v);
+    }
+  }
+  s_sum[rl][c] = acc;
+  __syncthreads();
+  if (rl == 0) part[(tile * gridDim.y + chunk) * kTileCols + c] = (s_sum[0][c] + s_sum[1][c]) +
+                                                                  (s_sum[2][c] + s_sum[3][c]);
+}
+
+// b_j = Pi_fp16(sum_i |W_ij| / M), 1 for an all-zero column; the chunks are
+// added in order.
+static __global__ void __launch_bounds__(kTileCols) colnorm_b_kernel(const double* __restrict__ part,
+                                                              int64_t n_chunks, int64_t M, int64_t N,
+                                                              uint16_t* __restrict__ b) {
+  const int64_t tile = blockIdx.x, j = tile * kTileCols + threadIdx.x;
+  if (j >= N) return;
+  double sum = 0.0;
+  for (int64_t k = 0; k < n_chunks; ++k) sum += part[(tile * n_chunks + k) * kTileCols + threadIdx.x];
+  const double bj = sum > 0.0 ? project<kScaleFp16>(sum / (double)M) : 1.0;
+  b[j] = encode_scale<kScaleFp16>(bj);
+}
+
+// a = Pi_Fa(max_{j in block} |W_ij / b_j| / qmax), 1 for a zero block; the
+// quotients are correctly rounded float64 divisions.
+template <int WT, int GRID, int AFMT, int G>
+__global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__ W, int64_t ldw,
+                                                        int64_t M, int64_t N,
+                                                        const uint16_t* __restrict__ b,
+                                                        void* __restrict__ a_) {
+  using AT = typename ScaleStore<AFMT>::T;
+  const int64_t nblk = N / G;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * nblk) return;
+  const int64_t row = idx / nblk, blk = idx - row * nblk;
+  double amax = 0.0;
+#pragma unroll
+  for (int c = 0; c < G / 8; ++c) {
+    float v[8];
+    load8<WT>(W, row * ldw + blk * G + 8 * c, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const double bj = (double)fp16_bits_to_float(b[blk * G + 8 * c + k]);
+      amax = __builtin_fmax(amax, (double)__builtin_fabsf(v[k]) / bj);
+    }
+  }
+  const double s = amax > 0.0 ? project<AFMT>(amax / (double)Grid<GRID>::qmax) : 1.0;
+  reinterpret_cast<AT*>(a_)[idx] = encode_scale<AFMT>(s);
+}
+
 // ------------------------------------------------------------ BCD pass
 
 constexpr int kThreads = 256;  // 4 waves
@@ -568,6 +639,21 @@ hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a
 }
 
 template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
+                               double* part, hipStream_t st) {
+  const int64_t n_tiles = (N + kTileCols - 1) / kTileCols;
+  const int64_t n_chunks = (M + kColnormRows - 1) / kColnormRows;
+  colnorm_partial_kernel<WT><<<dim3((unsigned)n_tiles, (unsigned)n_chunks), 256, 0, st>>>(W, ldw, M, N, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  colnorm_b_kernel<<<(unsigned)n_tiles, kTileCols, 0, st>>>(part, n_chunks, M, N, b);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  colnorm_a_kernel<WT, GRID, AFMT, G><<<blocks_for(M * (N / G), 256), 256, 0, st>>>(W, ldw, M, N, b, a);
+  return hipGetLastError();
+}
+
+template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
                           int n_iters, hipStream_t st) {
   // partial buffers alternate between passes: pass k reads the partials of
@@ -609,6 +695,8 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
 #define DQ_INST_WGA(WT, GR, AF, G)                                                               \
   template hipError_t launch_init<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, void*,  \
                                                  uint16_t*, hipStream_t);                         \
+  template hipError_t launch_init_colnorm<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, \
+                                                         void*, uint16_t*, double*, hipStream_t); \
   template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
                                                     const PassGeom&, int, hipStream_t);            \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \

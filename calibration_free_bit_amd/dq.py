@@ -24,7 +24,7 @@ GRID_INT4, GRID_E2M1 = 0, 1
 SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
-EXPORTS = ("dq_workspace_bytes", "dq_init_rtn", "dq_bcd_iterate", "dq_pack_codes",
+EXPORTS = ("dq_workspace_bytes", "dq_init_rtn", "dq_init_colnorm", "dq_bcd_iterate", "dq_pack_codes",
            "dq_rescale_quantize_act", "dq_status_string", "dq_abi_version")
 
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.dq_workspace_bytes.argtypes, L.dq_workspace_bytes.restype = [P], sz
         L.dq_init_rtn.argtypes, L.dq_init_rtn.restype = [P, vp, vp, vp, vp], ctypes.c_int
+        L.dq_init_colnorm.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.dq_init_colnorm.restype = ctypes.c_int
         L.dq_bcd_iterate.argtypes = [P, vp, vp, vp, i32, vp, sz, vp, vp]
         L.dq_bcd_iterate.restype = ctypes.c_int
         L.dq_pack_codes.argtypes, L.dq_pack_codes.restype = [P, vp, vp, vp, vp, vp], ctypes.c_int
@@ -130,6 +132,13 @@ def init_rtn(p: Problem, W, a, b, stream=None) -> None:
     _check("dq_init_rtn", lib().dq_init_rtn(ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), _stream(stream)))
 
 
+def init_colnorm(p: Problem, W, a, b, workspace, workspace_nbytes: int | None = None,
+                 stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check("dq_init_colnorm", lib().dq_init_colnorm(
+        ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), _ptr(workspace), int(nbytes), _stream(stream)))
+
+
 def bcd_iterate(p: Problem, W, a, b, n_iters: int, workspace, workspace_nbytes: int | None = None,
                 stats=None, stream=None) -> None:
     nbytes = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
@@ -179,6 +188,9 @@ class Solver:
 
     def init(self, stream=None):
         init_rtn(self.p, self.W, self.a, self.b, stream)
+
+    def init_colnorm(self, stream=None):
+        init_colnorm(self.p, self.W, self.a, self.b, self.ws, stream=stream)
 
     def iterate(self, n: int, stream=None):
         bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stream=stream)

@@ -82,8 +82,8 @@ typedef struct {
   int32_t group, grid, a_fmt, b_fmt, w_type, reserved;
 } dq_problem;
 
-/* Bytes of device workspace dq_bcd_iterate needs for problem p (0 if p is
- * invalid). Depends only on p's shape and format. */
+/* Bytes of device workspace dq_bcd_iterate and dq_init_colnorm need for
+ * problem p (0 if p is invalid). Depends only on p's shape and format. */
 size_t dq_workspace_bytes(const dq_problem* p);
 
 /* Absmax round-to-nearest initialization (DualQuant summary §3: symmetric
@@ -95,6 +95,21 @@ size_t dq_workspace_bytes(const dq_problem* p);
  *   b  out  [cols] fp16 bits */
 int dq_init_rtn(const dq_problem* p, const void* W, void* a, uint16_t* b,
                 void* stream);
+
+/* Column-norm initialization, the alternative starting point of the
+ * summary §5.3 (format-native row absmax scales together with per-column
+ * L1-norm scales; the page gives no formula, so the following is this
+ * library's reading): b_j = Pi_fp16(sum_i |W_ij| / rows) (1 for an all-zero
+ * column), then a[i, g] = Pi_Fa(max_{j in g} |W_ij / b_j| / qmax) with
+ * correctly rounded float64 quotients (1 for an all-zero block). Compared
+ * with dq_init_rtn it moves the column magnitudes into b, which keeps the
+ * block scales of small-valued formats such as NVFP4 out of E4M3's
+ * subnormal range. Deterministic: the column sums run in a fixed order.
+ *   W, a, b    as for dq_init_rtn
+ *   workspace  scratch of at least dq_workspace_bytes(p) bytes, 256-byte
+ *              aligned (the same workspace dq_bcd_iterate takes) */
+int dq_init_colnorm(const dq_problem* p, const void* W, void* a, uint16_t* b,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* n_iters BCD iterations from the state (a, b), in place (reproduction
  * README "Core equations" and its flowchart; summary §4.3, App. A-B).

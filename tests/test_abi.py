@@ -94,6 +94,19 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert L.dq_pack_codes(ctypes.byref(p), ok, ok, ctypes.c_void_p(258), ok, None) == dq.ERR_INVALID_ARG
 
 
+def test_init_colnorm_checks_arguments_before_launch():
+    L = dq.lib()
+    p = _p()
+    ok = ctypes.c_void_p(256)
+    need = L.dq_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert L.dq_init_colnorm(ctypes.byref(p), None, ok, ok, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_init_colnorm(ctypes.byref(p), ctypes.c_void_p(264), ok, ok, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_init_colnorm(ctypes.byref(p), ok, ok, ok, None, need, None) == dq.ERR_WORKSPACE
+    assert L.dq_init_colnorm(ctypes.byref(p), ok, ok, ok, ok, need - 1, None) == dq.ERR_WORKSPACE
+    assert L.dq_init_colnorm(ctypes.byref(p), ok, ok, ok, ctypes.c_void_p(128), need, None) == dq.ERR_WORKSPACE
+
+
 def test_iterate_checks_workspace_and_stats_before_launch():
     L = dq.lib()
     p = _p()

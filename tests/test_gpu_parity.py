@@ -149,6 +149,47 @@ def test_zero_slices():
         _check(data, fmt, 3, f"{name} zero slices")
 
 
+# ------------------------------------------------ column-norm initialization
+
+def _colnorm_run(data, fmt, iters, ldw=None):
+    g = GpuRun(data, fmt, ldw)
+    g.s.init_colnorm()
+    if iters:
+        g.s.iterate(iters)
+    g.s.pack()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("name", sorted(ALL_FORMATS))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_colnorm_init_every_format(name, dtype):
+    fmt = ALL_FORMATS[name]
+    ofmt = oracle_fmt(fmt)
+    data = _mat(197, 192 + fmt.group, 31, dtype=dtype)
+    print(f"[case] colnorm init {name} {dtype}", flush=True)
+    g = _colnorm_run(data, fmt, 0)
+    a0, b0 = D.init_colnorm(as_f64(data), ofmt)
+    np.testing.assert_array_equal(g.b, b0)
+    np.testing.assert_array_equal(g.a, a0)
+
+
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32"])
+def test_colnorm_init_then_iterate(name):
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    data = _mat(300, 512, 37)
+    data[:, 100] = 0                   # an all-zero column
+    data[7, 64:128] = 0                # an all-zero block
+    print(f"[case] colnorm init + 6 iterations {name}", flush=True)
+    g = _colnorm_run(data, fmt, 6)
+    W64 = as_f64(data)
+    a0, b0 = D.init_colnorm(W64, ofmt)
+    sol = D.solve(W64, ofmt, 6, a=a0, b=b0)
+    r = compare(W64, g.a, g.b, g.Q, sol, ofmt, f"colnorm {name}")
+    assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
+
+
 # ------------------------------------------------------------ state / determinism
 
 def test_iterations_compose_and_are_deterministic():
