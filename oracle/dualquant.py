@@ -75,7 +75,12 @@ class Format:
 INT4_G64 = Format("int4", 64, "fp16", "fp16")
 MXINT4_G32 = Format("int4", 32, "e8m0", "fp16")
 NVFP4_G16 = Format("e2m1", 16, "e4m3", "fp16")
-FORMATS = {"int4_g64": INT4_G64, "mxint4_g32": MXINT4_G32, "nvfp4_g16": NVFP4_G16}
+MXFP4_G32 = Format("e2m1", 32, "e8m0", "fp16")
+#: The 8-bit MX formats of [DQ summary] §G.2 (elements: see oracle.formats).
+MXINT8_G32 = Format("int8", 32, "e8m0", "fp16")
+MXFP8_G32 = Format("e4m3", 32, "e8m0", "fp16")
+FORMATS = {"int4_g64": INT4_G64, "mxint4_g32": MXINT4_G32, "nvfp4_g16": NVFP4_G16,
+           "mxfp4_g32": MXFP4_G32, "mxint8_g32": MXINT8_G32, "mxfp8_g32": MXFP8_G32}
 
 
 def _check(W: np.ndarray, fmt: Format) -> np.ndarray:
@@ -244,19 +249,25 @@ def solve(W, fmt: Format, iters: int, a=None, b=None, history: bool = False) -> 
 # --------------------------------------------------------------------------
 
 def pack_codes(Q, fmt: Format) -> np.ndarray:
-    """Two 4-bit codes per byte, low nibble = even column: [M, N/2] uint8.
+    """Codes in storage form. 4-bit grids: two codes per byte, low nibble =
+    even column, [M, N/2] uint8; 8-bit grids: one code per byte, [M, N].
 
     [DQ summary] App. I packs INT4 weights offline for deployment. INT4 codes
-    are two's complement; E2M1 codes are sign + level index.
+    are two's complement; E2M1 codes are sign + level index; int8 is two's
+    complement and E4M3 the FP8 byte.
     """
-    nib = F.element_nibbles(Q, fmt.grid)
-    if nib.shape[1] % 2:
+    codes = F.element_codes(Q, fmt.grid)
+    if F.CODE_BITS[fmt.grid] == 8:
+        return codes.astype(np.uint8)
+    if codes.shape[1] % 2:
         raise ValueError("packing needs an even number of columns")
-    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
 def unpack_codes(packed, fmt: Format) -> np.ndarray:
     packed = np.asarray(packed, dtype=np.uint8)
+    if F.CODE_BITS[fmt.grid] == 8:
+        return F.codes_to_values(packed, fmt.grid)
     lo = F.nibbles_to_values(packed & 0xF, fmt.grid)
     hi = F.nibbles_to_values(packed >> 4, fmt.grid)
     out = np.empty((packed.shape[0], packed.shape[1] * 2))
@@ -268,7 +279,7 @@ def unpack_codes(packed, fmt: Format) -> np.ndarray:
 def footprint_bytes(M: int, N: int, fmt: Format):
     """Bytes of the emitted artefacts: (packed codes, a, b)."""
     a_bytes = 2 if fmt.a_fmt == "fp16" else 1
-    return M * N // 2, M * (N // fmt.group) * a_bytes, N * 2
+    return M * N * F.CODE_BITS[fmt.grid] // 8, M * (N // fmt.group) * a_bytes, N * 2
 
 
 # --------------------------------------------------------------------------

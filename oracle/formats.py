@@ -30,6 +30,11 @@ Readings where the pages are silent (each is listed in the design doc):
   above the largest go to the largest (no zero, no infinity);
 * "f32" is an unconstrained scale (the identity); it exists only so that
   the printed int8 example, which uses an unrounded scale, can be checked.
+* 8-bit element grids ([DQ summary] §G.2 evaluates MXINT8 and MXFP8 without
+  defining their elements): MXINT8 uses the symmetric int8 range
+  [-127, 127] of [SQuant tutorial] Ch. 2; MXFP8 uses OCP E4M3FN elements
+  (all finite E4M3 values), rounded to the nearest value with ties to the
+  even code and saturated at 448.
 """
 
 from __future__ import annotations
@@ -48,7 +53,10 @@ INT_GRIDS = {"int4": (-8, 7), "int8": (-127, 127)}
 
 #: Largest magnitude of each grid; absmax init divides by this
 #: ([DQ summary] §3: the symmetric scale is max|W| / qmax).
-QMAX = {"int4": 7.0, "int8": 127.0, "e2m1": 6.0}
+QMAX = {"int4": 7.0, "int8": 127.0, "e2m1": 6.0, "e4m3": 448.0}
+
+#: Storage bits of one element code.
+CODE_BITS = {"int4": 4, "e2m1": 4, "int8": 8, "e4m3": 8}
 
 
 def round_int_grid(x: np.ndarray, grid: str) -> np.ndarray:
@@ -81,10 +89,36 @@ def round_e2m1(x: np.ndarray) -> np.ndarray:
     return np.where(x < 0, -mag, mag) + 0.0               # -0 -> +0
 
 
+def e4m3_levels() -> np.ndarray:
+    """Non-negative E4M3FN element values in code order (code 0 is zero)."""
+    vals, _ = _e4m3_table()
+    return np.concatenate([[0.0], vals])
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest-value projection onto the signed E4M3FN element grid.
+
+    The magnitude goes to the nearest non-negative E4M3 value by linear
+    distance, above 448 to 448; at an exact midpoint the value with the even
+    code wins. The sign is kept; zero is +0. Returns float64 grid values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    lv = e4m3_levels()
+    ax = np.minimum(np.abs(x), lv[-1])
+    hi = np.clip(np.searchsorted(lv, ax, side="left"), 1, len(lv) - 1)
+    lo = hi - 1
+    dlo, dhi = ax - lv[lo], lv[hi] - ax          # exact: neighbours within a factor of 2
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    mag = np.where(take_hi, lv[hi], lv[lo])
+    return np.where(x < 0, -mag, mag) + 0.0
+
+
 def round_to_grid(x: np.ndarray, grid: str) -> np.ndarray:
     """The black-box element quantizer q of [DQ repro] "Core equations"."""
     if grid == "e2m1":
         return round_e2m1(x)
+    if grid == "e4m3":
+        return round_e4m3(x)
     return round_int_grid(x, grid)
 
 
@@ -92,6 +126,9 @@ def grid_codes(grid: str) -> np.ndarray:
     """All values of an element grid, ascending."""
     if grid == "e2m1":
         return np.unique(np.concatenate([-E2M1_LEVELS, E2M1_LEVELS]))
+    if grid == "e4m3":
+        lv = e4m3_levels()
+        return np.unique(np.concatenate([-lv, lv]))
     lo, hi = INT_GRIDS[grid]
     return np.arange(lo, hi + 1, dtype=np.float64)
 
@@ -221,6 +258,38 @@ def element_nibbles(q: np.ndarray, grid: str) -> np.ndarray:
         sign = ((q < 0) & (q != 0)).astype(np.int64) << 3
         return (sign | idx).astype(np.uint8)
     raise ValueError(f"no 4-bit encoding for grid {grid}")
+
+
+def element_codes(q: np.ndarray, grid: str) -> np.ndarray:
+    """Storage code of each grid value: a nibble (see element_nibbles) for
+    the 4-bit grids; a byte for the 8-bit ones -- int8 two's complement, or
+    the E4M3FN byte (sign bit 7, zero stored as +0)."""
+    q = np.asarray(q, dtype=np.float64)
+    if CODE_BITS[grid] == 4:
+        return element_nibbles(q, grid)
+    if grid == "int8":
+        return (q.astype(np.int64) & 0xFF).astype(np.uint8)
+    if grid == "e4m3":
+        lv = e4m3_levels()
+        idx = np.searchsorted(lv, np.abs(q))
+        if not np.all(lv[np.clip(idx, 0, len(lv) - 1)] == np.abs(q)):
+            raise ValueError("not an E4M3 value")
+        sign = ((q < 0) & (q != 0)).astype(np.int64) << 7
+        return (sign | idx).astype(np.uint8)
+    raise ValueError(grid)
+
+
+def codes_to_values(code: np.ndarray, grid: str) -> np.ndarray:
+    """Inverse of ``element_codes``."""
+    if CODE_BITS[grid] == 4:
+        return nibbles_to_values(code, grid)
+    code = np.asarray(code).astype(np.int64) & 0xFF
+    if grid == "int8":
+        return np.where(code >= 128, code - 256, code).astype(np.float64)
+    if grid == "e4m3":
+        mag = e4m3_levels()[np.minimum(code & 0x7F, 126)]
+        return np.where(code & 0x80, -mag, mag) + 0.0
+    raise ValueError(grid)
 
 
 def nibbles_to_values(nib: np.ndarray, grid: str) -> np.ndarray:

@@ -189,3 +189,57 @@ def test_encode_decode_round_trip(fmt):
         np.testing.assert_array_equal(enc.view(np.float16).astype(np.float64), vals)
     with pytest.raises(ValueError):
         F.encode_scale(np.array([vals[1] * (1 + 1e-12)]), fmt)
+
+
+# ------------------------------------------------------ 8-bit element grids
+
+def test_int8_grid_rounds_half_even_and_clips_symmetric():
+    # [SQuant tutorial] Ch. 2: symmetric int8 spans [-127, 127]
+    x = np.array([-130.0, -127.5, -126.5, -0.5, 0.5, 1.5, 126.5, 127.4, 127.5, 300.0])
+    assert list(F.round_int_grid(x, "int8")) == [-127, -127, -126, 0, 0, 2, 126, 127, 127, 127]
+    assert F.grid_codes("int8")[0] == -127 and F.grid_codes("int8")[-1] == 127
+
+
+def _e4m3_brute(x):
+    vals = []
+    codes = []
+    for c in range(0x7F):                       # finite non-negative codes
+        e, m = c >> 3, c & 7
+        vals.append(m / 8 * 2.0 ** -6 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8))
+        codes.append(c)
+    vals, codes = np.array(vals), np.array(codes)
+    out = []
+    for xi in x:
+        ax = min(abs(xi), 448.0)
+        d = np.abs(vals - ax)
+        best = np.flatnonzero(d == d.min())
+        pick = [i for i in best if codes[i] % 2 == 0] or list(best)
+        v = vals[pick[0]]
+        out.append(-v if xi < 0 else v)
+    return np.array(out) + 0.0
+
+
+def test_e4m3_elements_match_brute_force_and_torch():
+    lv = F.e4m3_levels()
+    mids = (lv[1:] + lv[:-1]) / 2
+    x = np.concatenate([lv, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e3),
+                        RNG.uniform(-460, 460, 3000), RNG.normal(0, 0.01, 1000)])
+    x = np.concatenate([x, -x, [1e9, -1e9, 448.0, 449.0, 464.0]])
+    got = F.round_e4m3(x)
+    np.testing.assert_array_equal(got, _e4m3_brute(x))
+    # torch's float8_e4m3fn cast rounds to nearest even within range
+    inr = np.abs(x) <= 448.0
+    xf = x[inr].astype(np.float32)
+    ref = torch.from_numpy(xf).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(F.round_e4m3(xf.astype(np.float64)), ref + 0.0)
+    assert not np.signbit(F.round_e4m3(np.array([-1e-9])))[0]
+
+
+def test_8bit_code_round_trip():
+    for grid in ("int8", "e4m3"):
+        g = F.grid_codes(grid)
+        c = F.element_codes(g, grid)
+        np.testing.assert_array_equal(F.codes_to_values(c, grid), g)
+        assert len(np.unique(c)) == len(g)
+    assert list(F.element_codes(np.array([-127.0, -1.0, 5.0]), "int8")) == [0x81, 0xFF, 0x05]
+    assert list(F.element_codes(np.array([1.0, -1.0, 448.0, 0.0]), "e4m3")) == [0x38, 0xB8, 0x7E, 0x00]

@@ -24,7 +24,7 @@ from oracle import dualquant as D
 from oracle import formats as F
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FMTS = [D.INT4_G64, D.MXINT4_G32, D.NVFP4_G16]
+FMTS = [D.INT4_G64, D.MXINT4_G32, D.NVFP4_G16, D.MXFP4_G32, D.MXINT8_G32, D.MXFP8_G32]
 
 
 def _w(M, N, seed, std=0.02, outliers=(3, 20.0), dtype="bf16"):
@@ -87,10 +87,18 @@ def test_rtn_error_bound_half_step(fmt):
     if fmt.grid == "int4":
         inside = (x <= 7.5) & (x >= -8.5)
         half = step / 2
-    else:  # E2M1 spacing is 0.5 below 2, 1 below 4, 2 up to 6
+    elif fmt.grid == "int8":
+        inside = np.abs(x) <= 127.5
+        half = step / 2
+    elif fmt.grid == "e2m1":  # E2M1 spacing is 0.5 below 2, 1 below 4, 2 up to 6
         ax = np.abs(x)
         inside = ax <= 6
         half = step * np.where(ax < 2, 0.25, np.where(ax < 4, 0.5, 1.0))
+    else:  # E4M3 spacing is 2^(e-3) in binade [2^e, 2^(e+1)), 2^-9 below 2^-6
+        ax = np.abs(x)
+        inside = ax <= 448
+        e = np.floor(np.log2(np.maximum(ax, 2.0 ** -6)))
+        half = step * 2.0 ** (e - 3) / 2
     assert inside.mean() > 0.95      # E8M0 may round the scale down 1.5x
     assert np.all(err[inside] <= half[inside] * (1 + 1e-12))
 
@@ -98,7 +106,7 @@ def test_rtn_error_bound_half_step(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_t0_is_textbook_per_group_absmax_rtn(fmt):
     W = _w(8, 64, 4)
-    G, qmax = fmt.group, {"int4": 7, "e2m1": 6}[fmt.grid]
+    G, qmax = fmt.group, {"int4": 7, "e2m1": 6, "int8": 127, "e4m3": 448}[fmt.grid]
     s = D.solve(W, fmt, 0)
     for i in range(W.shape[0]):
         for g in range(W.shape[1] // G):
@@ -107,12 +115,27 @@ def test_t0_is_textbook_per_group_absmax_rtn(fmt):
             assert s.a[i, g] == scale
             for j, w in enumerate(blk):
                 t = w / scale
-                if fmt.grid == "int4":
-                    r = min(max(round(t), -8), 7)    # Python round: half to even
-                else:
+                if fmt.grid in ("int4", "int8"):
+                    lo, hi = (-8, 7) if fmt.grid == "int4" else (-127, 127)
+                    r = min(max(round(t), lo), hi)    # Python round: half to even
+                elif fmt.grid == "e2m1":
                     r = F.round_e2m1(np.array([t]))[0]
+                else:
+                    r = _e4m3_nearest(t)
                 assert s.Q[i, g * G + j] == r
     assert np.all(s.b == 1.0)
+
+
+def _e4m3_nearest(t):
+    # nearest E4M3 magnitude from the bit definition, ties to the even code
+    best = None
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        v = m / 8 * 2.0 ** -6 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+        d = abs(min(abs(t), 448.0) - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, v)
+    return (-best[1] if t < 0 else best[1]) + 0.0
 
 
 # ------------------------------------------- closed-form update = brute force
@@ -316,16 +339,17 @@ def _frac_project(x, fmt):
 
 
 def _frac_round(x, grid):
-    if grid == "int4":
+    if grid in ("int4", "int8"):
+        lo, hi = F.INT_GRIDS[grid]
         fl = x.numerator // x.denominator
         r = x - fl
         q = fl + 1 if r > Fraction(1, 2) else fl if r < Fraction(1, 2) else (fl if fl % 2 == 0 else fl + 1)
-        return Fraction(min(max(q, -8), 7))
-    lv = [Fraction(float(v)) for v in F.E2M1_LEVELS]
-    ax = abs(x)
+        return Fraction(min(max(q, lo), hi))
+    lv = [Fraction(float(v)) for v in (F.E2M1_LEVELS if grid == "e2m1" else F.e4m3_levels())]
+    ax = min(abs(x), lv[-1])
     d = [abs(ax - v) for v in lv]
     m = min(d)
-    c = [k for k in range(8) if d[k] == m]
+    c = [k for k in range(len(lv)) if d[k] == m]
     k = [k for k in c if k % 2 == 0][0] if len(c) > 1 else c[0]
     return -lv[k] if x < 0 else lv[k]
 
@@ -381,9 +405,14 @@ def test_pack_round_trip_and_low_nibble_is_even_column(fmt):
     W = _w(8, 64, 22)
     s = D.solve(W, fmt, 2)
     p = D.pack_codes(s.Q, fmt)
-    assert p.shape == (8, 32) and p.dtype == np.uint8
     np.testing.assert_array_equal(D.unpack_codes(p, fmt), s.Q)
-    np.testing.assert_array_equal(p & 0xF, F.element_nibbles(s.Q[:, 0::2], fmt.grid))
+    assert p.dtype == np.uint8
+    if F.CODE_BITS[fmt.grid] == 4:
+        assert p.shape == (8, 32)
+        np.testing.assert_array_equal(p & 0xF, F.element_nibbles(s.Q[:, 0::2], fmt.grid))
+    else:
+        assert p.shape == (8, 64)
+        np.testing.assert_array_equal(p, F.element_codes(s.Q, fmt.grid))
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -403,8 +432,15 @@ def test_activation_rescale_follows_the_factorization(fmt):
     # RTN error bound on the rescaled activations (nothing clips at init)
     step = D.expand_blocks(xs, fmt.group)
     ax = np.abs(Xb / step)
-    half = step * (0.5 if fmt.grid == "int4" else np.where(ax < 2, 0.25, np.where(ax < 4, 0.5, 1.0)))
-    ok = ax <= (7.5 if fmt.grid == "int4" else 6)
+    if fmt.grid in ("int4", "int8"):
+        half = step * 0.5
+        ok = ax <= (7.5 if fmt.grid == "int4" else 127.5)
+    elif fmt.grid == "e2m1":
+        half = step * np.where(ax < 2, 0.25, np.where(ax < 4, 0.5, 1.0))
+        ok = ax <= 6
+    else:
+        half = step * 2.0 ** (np.floor(np.log2(np.maximum(ax, 2.0 ** -6))) - 3) / 2
+        ok = ax <= 448
     assert ok.mean() > 0.95      # E8M0 may round the scale down 1.5x
     assert np.all(np.abs(Xb - rec)[ok] <= half[ok] * (1 + 1e-12))
     # and the scales are legal and positive

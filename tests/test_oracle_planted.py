@@ -164,3 +164,16 @@ def test_colnorm_block_scales_without_column_division_are_caught(monkeypatch):
         return a, b
     monkeypatch.setattr(D, "init_colnorm", bad)
     assert _fails(*_colnorm_pins())
+
+
+def test_e4m3_element_ties_away_from_zero_is_caught(monkeypatch):
+    def bad(x):
+        x = np.asarray(x, dtype=np.float64)
+        lv = F.e4m3_levels()
+        ax = np.minimum(np.abs(x), lv[-1])
+        hi = np.clip(np.searchsorted(lv, ax, side="left"), 1, len(lv) - 1)
+        lo = hi - 1
+        mag = np.where(lv[hi] - ax <= ax - lv[lo], lv[hi], lv[lo])    # ties go up
+        return np.where(x < 0, -mag, mag) + 0.0
+    monkeypatch.setattr(F, "round_e4m3", bad)
+    assert _fails((TF.test_e4m3_elements_match_brute_force_and_torch, {}))
