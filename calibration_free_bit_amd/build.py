@@ -42,6 +42,8 @@ def _units():
         ("dq_api.o", os.path.join(CSRC, "dq_api.hip"), []),
         ("dq_kernels_int4.o", k, ["-DDQ_GRID_INST=dq::kGridInt4"]),
         ("dq_kernels_e2m1.o", k, ["-DDQ_GRID_INST=dq::kGridE2M1"]),
+        ("dq_kernels_int8.o", k, ["-DDQ_GRID_INST=dq::kGridInt8"]),
+        ("dq_kernels_e4m3.o", k, ["-DDQ_GRID_INST=dq::kGridE4M3"]),
     ]
 
 

@@ -24,7 +24,9 @@ int elem_size(int32_t w_type) { return w_type == DQ_W_F32 ? 4 : 2; }
 int check_problem(const dq_problem* p) {
   if (!p) return DQ_ERR_INVALID_ARG;
   if (p->group != 16 && p->group != 32 && p->group != 64) return DQ_ERR_UNSUPPORTED;
-  if (p->grid != DQ_GRID_INT4 && p->grid != DQ_GRID_E2M1) return DQ_ERR_UNSUPPORTED;
+  if (p->grid != DQ_GRID_INT4 && p->grid != DQ_GRID_E2M1 && p->grid != DQ_GRID_INT8 &&
+      p->grid != DQ_GRID_E4M3)
+    return DQ_ERR_UNSUPPORTED;
   if (p->a_fmt != DQ_SCALE_FP16 && p->a_fmt != DQ_SCALE_E8M0 && p->a_fmt != DQ_SCALE_E4M3)
     return DQ_ERR_UNSUPPORTED;
   if (p->b_fmt != DQ_SCALE_FP16) return DQ_ERR_UNSUPPORTED;
@@ -95,6 +97,8 @@ int dispatch(const dq_problem& p, F&& f) {
     switch (p.grid) {
       case DQ_GRID_INT4: return by_afmt.template operator()<WT, dq::kGridInt4>();
       case DQ_GRID_E2M1: return by_afmt.template operator()<WT, dq::kGridE2M1>();
+      case DQ_GRID_INT8: return by_afmt.template operator()<WT, dq::kGridInt8>();
+      case DQ_GRID_E4M3: return by_afmt.template operator()<WT, dq::kGridE4M3>();
     }
     return DQ_ERR_UNSUPPORTED;
   };
@@ -170,8 +174,9 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
 int dq_pack_codes(const dq_problem* p, const void* W, const void* a, const uint16_t* b,
                   uint8_t* packed, void* stream) {
   if (int s = check_problem(p)) return s;
+  const bool byte_codes = p->grid == DQ_GRID_INT8 || p->grid == DQ_GRID_E4M3;
   if (!W || !a || !b || !packed || !aligned16(W) || !aligned16(b) ||
-      (reinterpret_cast<uintptr_t>(packed) & 7u))
+      (reinterpret_cast<uintptr_t>(packed) & (byte_codes ? 15u : 7u)))
     return DQ_ERR_INVALID_ARG;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {

@@ -32,12 +32,15 @@
 
 namespace dq {
 
-enum : int { kGridInt4 = 0, kGridE2M1 = 1 };
+enum : int { kGridInt4 = 0, kGridE2M1 = 1, kGridInt8 = 2, kGridE4M3 = 3 };
 enum : int { kScaleFp16 = 0, kScaleE8M0 = 1, kScaleE4M3 = 2 };
 enum : int { kWF32 = 0, kWBF16 = 1 };
 
-// |y - rint(y)| above this flags a possible misrounding (0.5 - 2^-17).
+// |y - rint(y)| above this flags a possible misrounding (0.5 - 2^-17), for
+// quotients up to 8.25; the int8 grid (quotients up to 127.25) uses
+// 0.5 - 2^-13. The estimate's relative error is below 7 * 2^-24.
 constexpr float kTieFlag = 0.5f - 0x1p-17f;
+constexpr float kTieFlag8 = 0.5f - 0x1p-13f;
 
 // ------------------------------------------------------------ scale codes
 
@@ -161,6 +164,7 @@ template <int GRID> struct Grid;
 
 template <> struct Grid<kGridInt4> {
   static constexpr float qmax = 7.0f;
+  static constexpr int kBits = 4;
   // Fast path: y ~= x. Returns the code; accumulates |y - code| (in units
   // of the grid step) into flag.
   __device__ static __forceinline__ float fast(float y, float& flag) {
@@ -203,21 +207,19 @@ template <> struct Grid<kGridInt4> {
     for (int k = 0; k < 8; ++k) w |= nibble(q[k]) << (4 * k);
     return w;
   }
+  // Store 8 codes (4 bytes, 4-byte aligned).
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    *reinterpret_cast<uint32_t*>(dst) = pack8(q);
+  }
 };
 
 template <> struct Grid<kGridE2M1> {
   static constexpr float qmax = 6.0f;
-  // In binade scale t = |y| * 2^s (s = 1 below 2, 0 below 4, -1 above) the
-  // E2M1 levels are consecutive integers and ties-to-even-encoding is
-  // ties-to-even on t. frexp_exp gives e with |y| in [2^(e-1), 2^e).
-  __device__ static __forceinline__ float fast(float y, float& flag) {
-    const float ay = __builtin_fminf(__builtin_fabsf(y), 6.25f);
-    const int s = max(-1, min(1, 2 - __builtin_amdgcn_frexp_expf(ay)));
-    const float t = __builtin_ldexpf(ay, s);
-    const float r = __builtin_rintf(t);
-    flag = __builtin_fmaxf(flag, __builtin_fabsf(t - r));
-    return __builtin_copysignf(__builtin_ldexpf(r, -s), y);
-  }
+  static constexpr int kBits = 4;
+  // Exact path. In binade scale t = |y| * 2^s (s = 1 below 2, 0 below 4, -1
+  // above) the E2M1 levels are consecutive integers and ties to the even
+  // encoding are ties to even on t. frexp_exp gives e with |y| in
+  // [2^(e-1), 2^e).
   __device__ static __forceinline__ float exact(float y, float w, float a, float b) {
     const float ay = __builtin_fminf(__builtin_fabsf(y), 6.25f);
     const int s = max(-1, min(1, 2 - __builtin_amdgcn_frexp_expf(ay)));
@@ -230,15 +232,6 @@ template <> struct Grid<kGridE2M1> {
     const float mag = __builtin_fminf(__builtin_ldexpf(k + up, -s), 6.0f);
     return __builtin_copysignf(mag, w);
   }
-  __device__ static __forceinline__ uint32_t nibble(float q) {
-    const float aq = __builtin_fabsf(q);
-    // level index: 0,.5,1,1.5 -> 0..3 ; 2,3 -> 4,5 ; 4 -> 6 ; 6 -> 7
-    const uint32_t idx = aq < 2.0f ? (uint32_t)(aq * 2.0f)
-                       : aq < 4.0f ? (uint32_t)aq + 2u
-                       : (aq < 5.0f ? 6u : 7u);
-    return idx | ((q < 0.0f) ? 8u : 0u);
-  }
-
   // gfx950's scaled FP4 conversion rounds a float32 to the nearest E2M1
   // level with ties to the even encoding and saturates at 6 -- the same
   // rule as exact() -- but keeps the sign of a zero result (code 8).
@@ -293,6 +286,120 @@ template <> struct Grid<kGridE2M1> {
     const uint32_t mag = w & 0x77777777u;
     const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;  // bit 3 set iff magnitude != 0
     return w & (0x77777777u | nonzero);
+  }
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    *reinterpret_cast<uint32_t*>(dst) = pack8(q);
+  }
+};
+
+template <> struct Grid<kGridInt8> {
+  static constexpr float qmax = 127.0f;
+  static constexpr int kBits = 8;
+  __device__ static __forceinline__ float fast(float y, float& flag) {
+    const float yc = __builtin_amdgcn_fmed3f(y, -127.25f, 127.25f);
+    const float q = __builtin_rintf(yc);
+    flag = __builtin_fmaxf(flag, __builtin_fabsf(yc - q));
+    return q;
+  }
+  // Exact path: y ~= x within 0.5; m*a is exact (m has at most 8 bits).
+  __device__ static __forceinline__ float exact(float y, float w, float a, float b) {
+    const float yc = __builtin_amdgcn_fmed3f(y, -127.25f, 127.25f);
+    const float k = __builtin_floorf(yc);
+    const float m = k + 0.5f;
+    const float d = __builtin_fmaf(-(m * a), b, w);   // sign of W - m a b, exact
+    const bool k_odd = ((int)k & 1) != 0;
+    const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
+    return __builtin_amdgcn_fmed3f(k + up, -127.0f, 127.0f);
+  }
+  template <int N>
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+    float flag = 0.0f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) q[e] = fast(y[e], flag);
+    return flag > kTieFlag8;
+  }
+  __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
+                                              int e) {
+    return __builtin_fabsf(__builtin_amdgcn_fmed3f(y[e], -127.25f, 127.25f) - q[e]) > kTieFlag8;
+  }
+  // Store 8 codes as two's complement bytes (8 bytes, 8-byte aligned).
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k >> 2] |= ((uint32_t)((int)q[k]) & 0xFFu) << (8 * (k & 3));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
+};
+
+// OCP E4M3FN elements. gfx950's FP8 conversion rounds a float32 to the
+// nearest E4M3 value with ties to the even code (checked over every value,
+// every midpoint and their float32 neighbours); magnitudes from just above
+// 464 on become NaN, so inputs are clamped to +-456, which rounds to 448.
+// A zero result keeps its sign (code 0x80), which storing clears.
+template <> struct Grid<kGridE4M3> {
+  static constexpr float qmax = 448.0f;
+  static constexpr int kBits = 8;
+  // Exact path: in binade [2^e, 2^(e+1)) (e >= -6; below that the subnormal
+  // step) the values are k * 2^(e-3) with k in [8, 16), the code parity is
+  // k's, and m*a is exact (m has at most 5 bits).
+  __device__ static __forceinline__ float exact(float y, float w, float a, float b) {
+    const float ay = __builtin_fminf(__builtin_fabsf(y), 456.0f);
+    const int e = max(__builtin_amdgcn_frexp_expf(ay) - 1, -6);
+    const float t = __builtin_ldexpf(ay, 3 - e);
+    const float k = __builtin_floorf(t);
+    const float m = __builtin_ldexpf(k + 0.5f, e - 3);
+    const float d = __builtin_fmaf(-(m * a), b, __builtin_fabsf(w));
+    const bool k_odd = ((int)k & 1) != 0;
+    const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
+    const float mag = __builtin_fminf(__builtin_ldexpf(k + up, e - 3), 448.0f);
+    return __builtin_copysignf(mag, w);
+  }
+  // Four codes into one word (element p in byte p).
+  __device__ static __forceinline__ uint32_t cvt4(const float* y) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+  }
+  // Codes of N estimates by the same two-ended certificate as E2M1: the
+  // exact quotient lies in [y (1 - 2^-20), y (1 + 2^-20)]; equal codes at
+  // both ends are its codes. diff[g] receives the differing bytes of group
+  // g of 4 elements.
+  template <int N>
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+    static_assert(N % 4 == 0, "groups of 4");
+    uint32_t any = 0u;
+#pragma unroll
+    for (int g = 0; g < N; g += 4) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float yc = __builtin_amdgcn_fmed3f(y[g + k], -456.0f, 456.0f);
+        lo[k] = yc * (1.0f - 0x1p-20f);
+        hi[k] = yc * (1.0f + 0x1p-20f);
+      }
+      const uint32_t wl = cvt4(lo), wh = cvt4(hi);
+      diff[g / 4] = wl ^ wh;
+      any |= wl ^ wh;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 r;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wl, 1.0f, false); q[g + 0] = r.x; q[g + 1] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wl, 1.0f, true);  q[g + 2] = r.x; q[g + 3] = r.y;
+    }
+    return any != 0u;
+  }
+  __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
+                                              int e) {
+    return ((diff[e >> 2] >> (8 * (e & 3))) & 0xFFu) != 0u;
+  }
+  // Store 8 codes as E4M3 bytes (exact values; a zero as +0), 8 bytes.
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    uint32_t w[2] = {cvt4(q), cvt4(q + 4)};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t mag = w[i] & 0x7F7F7F7Fu;
+      const uint32_t nonzero = (mag + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7 set iff magnitude != 0
+      w[i] &= 0x7F7F7F7Fu | nonzero;
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
   }
 };
 

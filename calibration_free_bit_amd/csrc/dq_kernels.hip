@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
-        uint32_t diff[LC / 8];
+        uint32_t diff[LC / 4];
         if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
           // only the element slots where some lane is near a midpoint
 #pragma unroll
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra;
         }
-        uint32_t diff[LC / 8];
+        uint32_t diff[LC / 4];
         if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
 #pragma unroll
           for (int bl = 0; bl < NB; ++bl)
@@ -510,7 +510,8 @@ static __global__ void __launch_bounds__(kTileCols)
 
 // ------------------------------------------------------------------ pack
 
-// One thread per (16 columns, kPackRows rows), 8 bytes out per row; the
+// One thread per (16 columns, kPackRows rows), 8 (4-bit codes) or 16
+// (8-bit codes) bytes out per row; the
 // column reciprocals are formed once per thread. Codes come from the float32
 // estimate of W/(a b) (reciprocals: relative error below 4 units of 2^-24);
 // a wave with any element near a rounding midpoint re-decides that row's
@@ -559,7 +560,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
 #pragma unroll
       for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
     }
-    uint32_t diff[2];
+    uint32_t diff[4];
     if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff))) {
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl)
@@ -568,8 +569,12 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
           if (wave_any(Grid<GRID>::near(y, q, diff, k)))
             q[k] = Grid<GRID>::exact(y[k], w[k], av[bl], bj[k]);
     }
-    const uint2 word = make_uint2(Grid<GRID>::pack8(q), Grid<GRID>::pack8(q + 8));
-    if (ok) *reinterpret_cast<uint2*>(packed + row * (N / 2) + col / 2) = word;
+    if (ok) {
+      constexpr int B = Grid<GRID>::kBits;  // 4: two codes per byte; 8: one
+      uint8_t* dst = packed + row * (N * B / 8) + col * B / 8;
+      Grid<GRID>::store8(dst, q);
+      Grid<GRID>::store8(dst + B, q + 8);
+    }
   }
 }
 
@@ -611,15 +616,15 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
   float y[8], q[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
-  uint32_t diff[1];
+  uint32_t diff[2];
   if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
   }
-  const uint32_t word = Grid<GRID>::pack8(q);
   if (live) {
-    reinterpret_cast<uint32_t*>(xq + t * (N / 2))[col / 8] = word;
+    constexpr int B = Grid<GRID>::kBits;
+    Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
     if ((threadIdx.x % LPB) == 0) reinterpret_cast<AT*>(xs_)[t * (N / G) + col / G] = encode_scale<AFMT>(s);
   }
 }
@@ -713,6 +718,8 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
 #ifndef DQ_GRID_INST
 DQ_INST(kGridInt4)
 DQ_INST(kGridE2M1)
+DQ_INST(kGridInt8)
+DQ_INST(kGridE4M3)
 #else
 DQ_INST(DQ_GRID_INST)
 #endif

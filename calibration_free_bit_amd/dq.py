@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("DQ_LIB_PATH", os.path.join(_HERE, "_lib", "libdq.so")
 
 # enums of dq.h
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
-GRID_INT4, GRID_E2M1 = 0, 1
+GRID_INT4, GRID_E2M1, GRID_INT8, GRID_E4M3 = 0, 1, 2, 3
 SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
@@ -46,13 +46,19 @@ class Format:
     def a_dtype(self):
         return torch.int16 if self.a_fmt == SCALE_FP16 else torch.uint8
 
+    @property
+    def code_bits(self) -> int:
+        return 8 if self.grid in (GRID_INT8, GRID_E4M3) else 4
 
-#: Formats of the DualQuant summary §3 (column scales are fp16 for all).
+
+#: Formats of the DualQuant summary §3 and §G.2 (column scales are fp16 for all).
 FORMATS = {
     "int4_g64": Format(GRID_INT4, 64, SCALE_FP16),
     "mxint4_g32": Format(GRID_INT4, 32, SCALE_E8M0),
     "nvfp4_g16": Format(GRID_E2M1, 16, SCALE_E4M3),
     "mxfp4_g32": Format(GRID_E2M1, 32, SCALE_E8M0),
+    "mxint8_g32": Format(GRID_INT8, 32, SCALE_E8M0),
+    "mxfp8_g32": Format(GRID_E4M3, 32, SCALE_E8M0),
 }
 
 
@@ -184,7 +190,7 @@ class Solver:
         if nb == 0:
             raise DQError("dq_workspace_bytes", ERR_SHAPE, "invalid problem")
         self.ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
-        self.packed = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+        self.packed = torch.empty((M, N * fmt.code_bits // 8), dtype=torch.uint8, device=dev)
 
     def init(self, stream=None):
         init_rtn(self.p, self.W, self.a, self.b, stream)

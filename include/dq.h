@@ -32,9 +32,13 @@
  *    bits, or one byte per scale (E8M0 biased exponent, E4M3 byte, OCP
  *    E4M3FN without sign). b is uint16 fp16 bits. Arrays are dense:
  *    a[i * (cols/G) + g], b[j].
- *  - Element codes are 4-bit: INT4 two's complement in [-8, 7], or E2M1
- *    (sign bit, then level index 0..7 of 0, .5, 1, 1.5, 2, 3, 4, 6).
- *    Packed rows hold cols/2 bytes; the low nibble is the even column.
+ *  - Element codes: INT4 two's complement in [-8, 7], or E2M1 (sign bit,
+ *    then level index 0..7 of 0, .5, 1, 1.5, 2, 3, 4, 6), two per byte:
+ *    packed rows hold cols/2 bytes and the low nibble is the even column.
+ *    The 8-bit grids of the MX formats the summary evaluates at 8 bits
+ *    (§G.2) store one code per byte (rows of cols bytes): INT8 two's
+ *    complement in [-127, 127], or an OCP E4M3FN byte (finite values,
+ *    saturating at 448). A zero code is always stored as +0.
  *  - Rounding: element codes round to nearest with ties to even (INT4) or
  *    to the even encoding (E2M1), decided on the exact quotient; scales are
  *    projected to the nearest legal value (ties to even for fp16 / E4M3,
@@ -63,7 +67,7 @@ typedef enum {
   DQ_ERR_HIP = -5          /* a kernel launch failed                     */
 } dq_status;
 
-typedef enum { DQ_GRID_INT4 = 0, DQ_GRID_E2M1 = 1 } dq_grid;
+typedef enum { DQ_GRID_INT4 = 0, DQ_GRID_E2M1 = 1, DQ_GRID_INT8 = 2, DQ_GRID_E4M3 = 3 } dq_grid;
 typedef enum { DQ_SCALE_FP16 = 0, DQ_SCALE_E8M0 = 1, DQ_SCALE_E4M3 = 2 } dq_scale_fmt;
 typedef enum { DQ_W_F32 = 0, DQ_W_BF16 = 1 } dq_wtype;
 
@@ -75,8 +79,10 @@ typedef enum { DQ_W_F32 = 0, DQ_W_BF16 = 1 } dq_wtype;
  *   a_fmt       dq_scale_fmt of the block scales
  *   b_fmt       dq_scale_fmt of the column scales (only DQ_SCALE_FP16)
  *   w_type      dq_wtype of W and of X (float32 or bf16)
- * Formats of the DualQuant summary §3: INT4 {grid INT4, G 64, fp16},
- * MXINT4 {INT4, 32, E8M0}, NVFP4 {E2M1, 16, E4M3}, MXFP4 {E2M1, 32, E8M0}. */
+ * Formats of the DualQuant summary §3 and §G.2: INT4 {grid INT4, G 64,
+ * fp16}, MXINT4 {INT4, 32, E8M0}, NVFP4 {E2M1, 16, E4M3}, MXFP4 {E2M1, 32,
+ * E8M0}, MXINT8 {INT8, 32, E8M0}, MXFP8 {E4M3, 32, E8M0}; every grid x
+ * group x block-scale combination is accepted. */
 typedef struct {
   int64_t rows, cols, ldw;
   int32_t group, grid, a_fmt, b_fmt, w_type, reserved;
@@ -89,7 +95,8 @@ size_t dq_workspace_bytes(const dq_problem* p);
 /* Absmax round-to-nearest initialization (DualQuant summary §3: symmetric
  * scale max|W| / qmax per block of G contiguous row elements; §5.3:
  * format-native row absmax scales). Writes a[i, g] = Pi_Fa(absmax / qmax)
- * (qmax 7 for INT4, 6 for E2M1; 1 for an all-zero block) and b[j] = 1.
+ * (qmax 7 for INT4, 6 for E2M1, 127 for INT8, 448 for E4M3; 1 for an
+ * all-zero block) and b[j] = 1.
  *   W  in   [rows, ldw] of w_type
  *   a  out  [rows, cols/G] in a_fmt's encoding
  *   b  out  [cols] fp16 bits */
@@ -131,7 +138,8 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
 /* Final codes Q = q(W/(a b)), packed two per byte (summary App. I: packed
  * offline for deployment).
  *   b       in   [cols] fp16 bits, 16-byte aligned
- *   packed  out  [rows, cols/2] uint8, row pitch cols/2, 8-byte aligned */
+ *   packed  out  4-bit grids: [rows, cols/2] uint8, row pitch cols/2,
+ *                8-byte aligned; 8-bit grids: [rows, cols], 16-byte aligned */
 int dq_pack_codes(const dq_problem* p, const void* W, const void* a,
                   const uint16_t* b, uint8_t* packed, void* stream);
 
@@ -145,7 +153,8 @@ int dq_pack_codes(const dq_problem* p, const void* W, const void* a,
  *                  are used; base and row pitch 16-byte aligned
  *   tokens    number of rows of X (>= 0; 0 is a no-op)
  *   b         in   [cols] fp16 bits, 16-byte aligned
- *   xq        out  [tokens, cols/2] packed codes, 16-byte aligned
+ *   xq        out  [tokens, cols/2] (4-bit grids) or [tokens, cols] (8-bit)
+ *                  codes, 16-byte aligned
  *   x_scales  out  [tokens, cols/G] in a_fmt's encoding */
 int dq_rescale_quantize_act(const dq_problem* p, const void* X, int64_t tokens,
                             int64_t ldx, const uint16_t* b, uint8_t* xq,

@@ -10,12 +10,12 @@ from calibration_free_bit_amd import dq
 from oracle import dualquant as D
 from oracle import formats as F
 
-GRID_NAME = {dq.GRID_INT4: "int4", dq.GRID_E2M1: "e2m1"}
+GRID_NAME = {dq.GRID_INT4: "int4", dq.GRID_E2M1: "e2m1", dq.GRID_INT8: "int8", dq.GRID_E4M3: "e4m3"}
 AFMT_NAME = {dq.SCALE_FP16: "fp16", dq.SCALE_E8M0: "e8m0", dq.SCALE_E4M3: "e4m3"}
 
 #: Every (grid, G, block-scale) combination the library builds, by name.
 ALL_FORMATS = {f"{GRID_NAME[g]}_g{G}_{AFMT_NAME[a]}": dq.Format(g, G, a)
-               for g in (dq.GRID_INT4, dq.GRID_E2M1) for G in (16, 32, 64)
+               for g in (dq.GRID_INT4, dq.GRID_E2M1, dq.GRID_INT8, dq.GRID_E4M3) for G in (16, 32, 64)
                for a in (dq.SCALE_FP16, dq.SCALE_E8M0, dq.SCALE_E4M3)}
 
 

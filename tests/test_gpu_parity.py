@@ -20,8 +20,8 @@ from tests.gpu_util import ALL_FORMATS, GpuRun, as_f64, compare, oracle_fmt
 
 pytestmark = pytest.mark.gpu
 
-NAMED = {"int4_g64": dq.FORMATS["int4_g64"], "mxint4_g32": dq.FORMATS["mxint4_g32"],
-         "nvfp4_g16": dq.FORMATS["nvfp4_g16"], "mxfp4_g32": dq.FORMATS["mxfp4_g32"]}
+NAMED = {k: dq.FORMATS[k] for k in ("int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32",
+                                    "mxint8_g32", "mxfp8_g32")}
 
 
 def _mat(M, N, seed, dtype="bf16", std=0.02, n_out=3, fac=20.0):
@@ -79,18 +79,21 @@ def test_padded_leading_dimension():
         _check(data, NAMED[name], 3, f"{name} ldw 256", ldw=256)
 
 
-def test_exact_ties_power_of_two_scales():
-    # E8M0 block scales with b = 1 put many W / a exactly on half-integers:
-    # the tie rule (half to even) decides them on both sides.
+@pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32", "mxfp8_g32"])
+def test_exact_ties_power_of_two_scales(name):
+    # E8M0 block scales with b = 1 put many W / a exactly on grid midpoints
+    # (half-integers, or E4M3 midpoints): the tie rule (to the even code)
+    # decides them on both sides.
     data = _mat(256, 256, 9, n_out=0)
-    fmt = NAMED["mxint4_g32"]
+    fmt = NAMED[name]
     g = GpuRun(data, fmt).run(0)
     W64 = as_f64(data)
     sol = D.solve(W64, oracle_fmt(fmt), 0)
     ties = D.code_ties(W64, sol.a, sol.b, oracle_fmt(fmt))
     assert ties.sum() > 100
     np.testing.assert_array_equal(g.Q, sol.Q)
-    _check(data, fmt, 3, "mxint4 ties iterated")
+    np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, oracle_fmt(fmt)))
+    _check(data, fmt, 3, f"{name} ties iterated")
 
 
 def test_exact_ties_e2m1_power_of_two_scales():
@@ -174,7 +177,8 @@ def test_colnorm_init_every_format(name, dtype):
     np.testing.assert_array_equal(g.a, a0)
 
 
-@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32"])
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32", "mxint8_g32",
+                                  "mxfp8_g32"])
 def test_colnorm_init_then_iterate(name):
     fmt = NAMED[name]
     ofmt = oracle_fmt(fmt)
@@ -207,7 +211,7 @@ def test_iterations_compose_and_are_deterministic():
 
 # ------------------------------------------------------------ packing / activations
 
-@pytest.mark.parametrize("name", ["int4_g64", "nvfp4_g16", "mxint4_g32"])
+@pytest.mark.parametrize("name", ["int4_g64", "nvfp4_g16", "mxint4_g32", "mxint8_g32", "mxfp8_g32"])
 def test_packed_bytes_equal_oracle_packing(name):
     fmt = NAMED[name]
     data = _mat(96, 256, 21)
@@ -216,7 +220,8 @@ def test_packed_bytes_equal_oracle_packing(name):
     np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, oracle_fmt(fmt)))
 
 
-@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32"])
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxfp4_g32", "mxint8_g32",
+                                  "mxfp8_g32"])
 @pytest.mark.parametrize("tokens", [1, 37, 256])
 def test_activation_rescale_quantize(name, tokens):
     fmt = NAMED[name]
@@ -226,7 +231,7 @@ def test_activation_rescale_quantize(name, tokens):
     g = GpuRun(data, fmt).run(2)                       # b from a real solve
     X = synth.make_activations(tokens, N, 29)
     Xd = torch.from_numpy(X.view(np.int16)).cuda()
-    xq = torch.empty((tokens, N // 2), dtype=torch.uint8, device="cuda")
+    xq = torch.empty((tokens, N * fmt.code_bits // 8), dtype=torch.uint8, device="cuda")
     xs = torch.empty((tokens, N // fmt.group), dtype=fmt.a_dtype, device="cuda")
     dq.rescale_quantize_act(g.s.p, Xd, tokens, N, g.s.b, xq, xs)
     torch.cuda.synchronize()

@@ -24,21 +24,24 @@ from tests.gpu_util import decode_a, decode_b, oracle_fmt
 
 pytestmark = pytest.mark.gpu
 
-GRID_NAME = {dq.GRID_INT4: "int4", dq.GRID_E2M1: "e2m1"}
+GRID_NAME = {dq.GRID_INT4: "int4", dq.GRID_E2M1: "e2m1", dq.GRID_INT8: "int8", dq.GRID_E4M3: "e4m3"}
 
 
-def _nibble_table(grid: int) -> torch.Tensor:
-    return torch.tensor(F.nibbles_to_values(np.arange(16), GRID_NAME[grid]), dtype=torch.float32,
+def _code_table(fmt) -> torch.Tensor:
+    n = 1 << fmt.code_bits
+    return torch.tensor(F.codes_to_values(np.arange(n), GRID_NAME[fmt.grid]), dtype=torch.float32,
                         device="cuda")
 
 
-def _unpack(packed: torch.Tensor, table: torch.Tensor) -> torch.Tensor:
+def _unpack(packed: torch.Tensor, table: torch.Tensor, bits: int) -> torch.Tensor:
+    if bits == 8:
+        return table[packed.long()]
     lo = table[(packed & 0xF).long()]
     hi = table[(packed >> 4).long()]
     return torch.stack([lo, hi], dim=-1).reshape(packed.shape[0], packed.shape[1] * 2)
 
 
-@pytest.mark.parametrize("name", ["int4_g64", "nvfp4_g16", "mxfp4_g32"])
+@pytest.mark.parametrize("name", ["int4_g64", "nvfp4_g16", "mxfp4_g32", "mxint8_g32", "mxfp8_g32"])
 def test_w4a4_product_matches_factorization(name):
     fmt = dq.FORMATS[name]
     ofmt = oracle_fmt(fmt)
@@ -52,14 +55,14 @@ def test_w4a4_product_matches_factorization(name):
     s.solve(10)
     Xh = synth.make_activations(T, N, 6)
     X = torch.from_numpy(Xh.view(np.int16)).cuda()
-    xq = torch.empty((T, N // 2), dtype=torch.uint8, device="cuda")
+    xq = torch.empty((T, N * fmt.code_bits // 8), dtype=torch.uint8, device="cuda")
     xs = torch.empty((T, N // G), dtype=fmt.a_dtype, device="cuda")
     dq.rescale_quantize_act(s.p, X, T, N, s.b, xq, xs)
     torch.cuda.synchronize()
 
-    table = _nibble_table(fmt.grid)
-    Qw = _unpack(s.packed, table)                          # [M, N] codes as values
-    Qx = _unpack(xq, table)                                # [T, N]
+    table = _code_table(fmt)
+    Qw = _unpack(s.packed, table, fmt.code_bits)           # [M, N] codes as values
+    Qx = _unpack(xq, table, fmt.code_bits)                 # [T, N]
     a = torch.from_numpy(decode_a(s.a, fmt)).float().cuda()          # [M, N/G]
     sx = torch.from_numpy(decode_a(xs, fmt)).float().cuda()          # [T, N/G]
 
