@@ -68,7 +68,9 @@ Workspace pass_geometry(const dq_problem* p) {
   const size_t pass_bytes = 2 * size_t(g.n_tiles) * size_t(g.max_seg) * dq::kTileCols * 2 * sizeof(double);
   const size_t init_bytes = size_t(g.n_tiles) * size_t(ceil_div(p->rows, dq::kColnormRows)) *
                             dq::kTileCols * sizeof(double);
-  w.bytes = align256(std::max(pass_bytes, init_bytes));
+  // the report uses [workgroups][3] float64
+  const size_t report_bytes = size_t(dq::report_workgroups(p->rows, p->cols)) * 3 * sizeof(double);
+  w.bytes = align256(std::max({pass_bytes, init_bytes, report_bytes}));
   return w;
 }
 
@@ -181,6 +183,27 @@ int dq_pack_codes(const dq_problem* p, const void* W, const void* a, const uint1
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
     return hip_status(dq::launch_pack<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, packed, st));
+  });
+}
+
+int dq_quant_report(const dq_problem* p, const void* W, const void* a, const uint16_t* b,
+                    const uint8_t* prev_packed, uint8_t* packed, double* report, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (int s = check_problem(p)) return s;
+  const uintptr_t code_align = (p->grid == DQ_GRID_INT8 || p->grid == DQ_GRID_E4M3) ? 15u : 7u;
+  if (!W || !a || !b || !report || !aligned16(W) || !aligned16(b) ||
+      (reinterpret_cast<uintptr_t>(packed) & code_align) ||
+      (reinterpret_cast<uintptr_t>(prev_packed) & code_align) ||
+      (reinterpret_cast<uintptr_t>(report) & 7u))
+    return DQ_ERR_INVALID_ARG;
+  const Workspace ws = pass_geometry(p);
+  if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DQ_ERR_WORKSPACE;
+  double* part = static_cast<double*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_report<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, prev_packed,
+                                                       packed, report, part, st));
   });
 }
 

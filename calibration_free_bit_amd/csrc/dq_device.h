@@ -162,6 +162,15 @@ __device__ __forceinline__ float ls_scale_fast(double num, double den, bool& uns
 
 template <int GRID> struct Grid;
 
+// Number of non-zero nibbles / bytes of x.
+__device__ __forceinline__ int nibbles_differ(uint32_t x) {
+  return __builtin_popcount((x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x11111111u);
+}
+__device__ __forceinline__ int bytes_differ(uint32_t x) {
+  x |= x >> 4;
+  return __builtin_popcount((x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x01010101u);
+}
+
 template <> struct Grid<kGridInt4> {
   static constexpr float qmax = 7.0f;
   static constexpr int kBits = 4;
@@ -207,9 +216,13 @@ template <> struct Grid<kGridInt4> {
     for (int k = 0; k < 8; ++k) w |= nibble(q[k]) << (4 * k);
     return w;
   }
+  // 8 codes in storage form, and the number of codes two such words differ in.
+  using Word = uint32_t;
+  __device__ static __forceinline__ Word encode8(const float* q) { return pack8(q); }
+  __device__ static __forceinline__ int count_diff(Word x, Word y) { return nibbles_differ(x ^ y); }
   // Store 8 codes (4 bytes, 4-byte aligned).
   __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
-    *reinterpret_cast<uint32_t*>(dst) = pack8(q);
+    *reinterpret_cast<Word*>(dst) = encode8(q);
   }
 };
 
@@ -287,8 +300,11 @@ template <> struct Grid<kGridE2M1> {
     const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;  // bit 3 set iff magnitude != 0
     return w & (0x77777777u | nonzero);
   }
+  using Word = uint32_t;
+  __device__ static __forceinline__ Word encode8(const float* q) { return pack8(q); }
+  __device__ static __forceinline__ int count_diff(Word x, Word y) { return nibbles_differ(x ^ y); }
   __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
-    *reinterpret_cast<uint32_t*>(dst) = pack8(q);
+    *reinterpret_cast<Word*>(dst) = encode8(q);
   }
 };
 
@@ -322,12 +338,19 @@ template <> struct Grid<kGridInt8> {
                                               int e) {
     return __builtin_fabsf(__builtin_amdgcn_fmed3f(y[e], -127.25f, 127.25f) - q[e]) > kTieFlag8;
   }
-  // Store 8 codes as two's complement bytes (8 bytes, 8-byte aligned).
-  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+  // 8 codes as two's complement bytes (8 bytes, 8-byte aligned when stored).
+  using Word = uint2;
+  __device__ static __forceinline__ Word encode8(const float* q) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) w[k >> 2] |= ((uint32_t)((int)q[k]) & 0xFFu) << (8 * (k & 3));
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    return make_uint2(w[0], w[1]);
+  }
+  __device__ static __forceinline__ int count_diff(Word x, Word y) {
+    return bytes_differ(x.x ^ y.x) + bytes_differ(x.y ^ y.y);
+  }
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    *reinterpret_cast<Word*>(dst) = encode8(q);
   }
 };
 
@@ -390,8 +413,9 @@ template <> struct Grid<kGridE4M3> {
                                               int e) {
     return ((diff[e >> 2] >> (8 * (e & 3))) & 0xFFu) != 0u;
   }
-  // Store 8 codes as E4M3 bytes (exact values; a zero as +0), 8 bytes.
-  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+  // 8 codes as E4M3 bytes (exact values; a zero as +0), 8 bytes.
+  using Word = uint2;
+  __device__ static __forceinline__ Word encode8(const float* q) {
     uint32_t w[2] = {cvt4(q), cvt4(q + 4)};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -399,7 +423,13 @@ template <> struct Grid<kGridE4M3> {
       const uint32_t nonzero = (mag + 0x7F7F7F7Fu) & 0x80808080u;  // bit 7 set iff magnitude != 0
       w[i] &= 0x7F7F7F7Fu | nonzero;
     }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    return make_uint2(w[0], w[1]);
+  }
+  __device__ static __forceinline__ int count_diff(Word x, Word y) {
+    return bytes_differ(x.x ^ y.x) + bytes_differ(x.y ^ y.y);
+  }
+  __device__ static __forceinline__ void store8(uint8_t* dst, const float* q) {
+    *reinterpret_cast<Word*>(dst) = encode8(q);
   }
 };
 

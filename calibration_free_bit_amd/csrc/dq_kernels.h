@@ -39,6 +39,18 @@ template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                                double* part, hipStream_t st);
 
+// Rows per thread of the packing / report kernel, and the report kernel's
+// workgroups (256 threads; one float64 triple each in the workspace).
+constexpr int kPackRows = 4;
+inline int64_t report_workgroups(int64_t M, int64_t N) {
+  return (((M + kPackRows - 1) / kPackRows) * (N / 16) + 255) / 256;
+}
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_report(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
+                         const uint16_t* b, const uint8_t* prev, uint8_t* packed, double* report,
+                         double* part, hipStream_t st);
+
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                        hipStream_t st);

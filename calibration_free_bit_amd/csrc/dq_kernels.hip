@@ -511,21 +511,29 @@ static __global__ void __launch_bounds__(kTileCols)
 // ------------------------------------------------------------------ pack
 
 // One thread per (16 columns, kPackRows rows), 8 (4-bit codes) or 16
-// (8-bit codes) bytes out per row; the
-// column reciprocals are formed once per thread. Codes come from the float32
-// estimate of W/(a b) (reciprocals: relative error below 4 units of 2^-24);
-// a wave with any element near a rounding midpoint re-decides that row's
-// codes exactly, as the pass kernel does.
-constexpr int kPackRows = 4;
-
-template <int WT, int GRID, int AFMT, int G>
+// (8-bit codes) bytes out per row; the column reciprocals are formed once
+// per thread. Codes come from the float32 estimate of W/(a b) (reciprocals:
+// relative error below 4 units of 2^-24); a wave with any element near a
+// rounding midpoint re-decides those element slots exactly, as the pass
+// kernel does.
+//
+// With REPORT the kernel also measures the state: per workgroup it writes
+// the float64 sums of (W - a Q b)^2 and W^2 and the number of codes that
+// differ from prev (if given) to part[blockIdx.x][3]; packed may then be
+// null. Each thread sums its elements in order, then the workgroup adds the
+// threads in a fixed tree, so the result does not depend on timing.
+template <int WT, int GRID, int AFMT, int G, bool REPORT>
 __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, int64_t ldw,
                                                    int64_t M, int64_t N, const void* __restrict__ a_,
                                                    const uint16_t* __restrict__ b,
-                                                   uint8_t* __restrict__ packed) {
+                                                   uint8_t* __restrict__ packed,
+                                                   const uint8_t* __restrict__ prev,
+                                                   double* __restrict__ part) {
   using AT = typename ScaleStore<AFMT>::T;
+  using Word = typename Grid<GRID>::Word;
   constexpr int BL = G < 16 ? G : 16;  // elements of one block in this thread
   constexpr int NB = 16 / BL;
+  constexpr int B = Grid<GRID>::kBits;  // 4: two codes per byte; 8: one
   const int64_t nch = N / 16;
   const int64_t n_rg = (M + kPackRows - 1) / kPackRows;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -541,6 +549,8 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
     bj[k] = fp16_bits_to_float((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));
     rb[k] = __builtin_amdgcn_rcpf(bj[k]);
   }
+  double sse = 0.0, w2 = 0.0;
+  int changed = 0;
 #pragma unroll
   for (int r = 0; r < kPackRows; ++r) {
     const int64_t row_raw = rg * kPackRows + r;
@@ -569,13 +579,63 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
           if (wave_any(Grid<GRID>::near(y, q, diff, k)))
             q[k] = Grid<GRID>::exact(y[k], w[k], av[bl], bj[k]);
     }
-    if (ok) {
-      constexpr int B = Grid<GRID>::kBits;  // 4: two codes per byte; 8: one
+    const Word c0 = Grid<GRID>::encode8(q), c1 = Grid<GRID>::encode8(q + 8);
+    if (ok && (!REPORT || packed)) {
       uint8_t* dst = packed + row * (N * B / 8) + col * B / 8;
-      Grid<GRID>::store8(dst, q);
-      Grid<GRID>::store8(dst + B, q + 8);
+      *reinterpret_cast<Word*>(dst) = c0;
+      *reinterpret_cast<Word*>(dst + B) = c1;
+    }
+    if constexpr (REPORT) {
+      if (ok) {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+          for (int k = bl * BL; k < (bl + 1) * BL; ++k) {
+            // a Q b is exact in float64: q b is exact in float32
+            const double wk = (double)w[k];
+            const double d = wk - (double)(q[k] * bj[k]) * (double)av[bl];
+            sse = __builtin_fma(d, d, sse);
+            w2 = __builtin_fma(wk, wk, w2);
+          }
+        if (prev) {
+          const uint8_t* src = prev + row * (N * B / 8) + col * B / 8;
+          changed += Grid<GRID>::count_diff(c0, *reinterpret_cast<const Word*>(src)) +
+                     Grid<GRID>::count_diff(c1, *reinterpret_cast<const Word*>(src + B));
+        }
+      }
     }
   }
+  if constexpr (REPORT) {
+    __shared__ double s_part[3][256];
+    s_part[0][threadIdx.x] = sse;
+    s_part[1][threadIdx.x] = w2;
+    s_part[2][threadIdx.x] = (double)changed;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+      if ((int)threadIdx.x < h)
+        for (int i = 0; i < 3; ++i) s_part[i][threadIdx.x] += s_part[i][threadIdx.x + h];
+      __syncthreads();
+    }
+    if (threadIdx.x < 3) part[(int64_t)blockIdx.x * 3 + threadIdx.x] = s_part[threadIdx.x][0];
+  }
+}
+
+// Adds the per-workgroup report sums in a fixed order: thread t takes the
+// workgroups t, t + 256, ... in turn, then a fixed tree over the threads.
+static __global__ void __launch_bounds__(256) report_reduce_kernel(const double* __restrict__ part,
+                                                                   int64_t n, double* __restrict__ out) {
+  __shared__ double s_part[3][256];
+  double acc[3] = {0.0, 0.0, 0.0};
+  for (int64_t k = threadIdx.x; k < n; k += 256)
+    for (int i = 0; i < 3; ++i) acc[i] += part[k * 3 + i];
+  for (int i = 0; i < 3; ++i) s_part[i][threadIdx.x] = acc[i];
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h)
+      for (int i = 0; i < 3; ++i) s_part[i][threadIdx.x] += s_part[i][threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x < 3) out[threadIdx.x] = s_part[threadIdx.x][0];
 }
 
 // ------------------------------------------------------- activation side
@@ -682,8 +742,21 @@ template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
                        const uint16_t* b, uint8_t* packed, hipStream_t st) {
   const int64_t n_rg = (M + kPackRows - 1) / kPackRows;
-  pack_kernel<WT, GRID, AFMT, G><<<blocks_for(n_rg * (N / 16), 256), 256, 0, st>>>(W, ldw, M, N, a, b,
-                                                                                packed);
+  pack_kernel<WT, GRID, AFMT, G, false><<<blocks_for(n_rg * (N / 16), 256), 256, 0, st>>>(
+      W, ldw, M, N, a, b, packed, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int WT, int GRID, int AFMT, int G>
+hipError_t launch_report(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,
+                         const uint16_t* b, const uint8_t* prev, uint8_t* packed, double* report,
+                         double* part, hipStream_t st) {
+  const int64_t n_wg = report_workgroups(M, N);
+  pack_kernel<WT, GRID, AFMT, G, true><<<(unsigned)n_wg, 256, 0, st>>>(W, ldw, M, N, a, b, packed, prev,
+                                                                       part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  report_reduce_kernel<<<1, 256, 0, st>>>(part, n_wg, report);
   return hipGetLastError();
 }
 
@@ -706,7 +779,10 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
                                                     const PassGeom&, int, hipStream_t);            \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
                                                  const void*, const uint16_t*, uint8_t*,          \
-                                                 hipStream_t);
+                                                 hipStream_t);                                    \
+  template hipError_t launch_report<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,        \
+                                                   const void*, const uint16_t*, const uint8_t*,  \
+                                                   uint8_t*, double*, double*, hipStream_t);
 #define DQ_INST_GA(GR, AF, G)                                                                    \
   DQ_INST_WGA(kWF32, GR, AF, G)                                                                  \
   DQ_INST_WGA(kWBF16, GR, AF, G)                                                                 \

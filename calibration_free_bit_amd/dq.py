@@ -25,7 +25,7 @@ SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
 EXPORTS = ("dq_workspace_bytes", "dq_init_rtn", "dq_init_colnorm", "dq_bcd_iterate", "dq_pack_codes",
-           "dq_rescale_quantize_act", "dq_status_string", "dq_abi_version")
+           "dq_quant_report", "dq_rescale_quantize_act", "dq_status_string", "dq_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.dq_bcd_iterate.argtypes = [P, vp, vp, vp, i32, vp, sz, vp, vp]
         L.dq_bcd_iterate.restype = ctypes.c_int
         L.dq_pack_codes.argtypes, L.dq_pack_codes.restype = [P, vp, vp, vp, vp, vp], ctypes.c_int
+        L.dq_quant_report.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dq_quant_report.restype = ctypes.c_int
         L.dq_rescale_quantize_act.argtypes = [P, vp, i64, i64, vp, vp, vp, vp]
         L.dq_rescale_quantize_act.restype = ctypes.c_int
         L.dq_status_string.argtypes, L.dq_status_string.restype = [ctypes.c_int], ctypes.c_char_p
@@ -158,6 +160,14 @@ def pack_codes(p: Problem, W, a, b, packed, stream=None) -> None:
         ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), _ptr(packed), _stream(stream)))
 
 
+def quant_report(p: Problem, W, a, b, prev_packed, packed, report, workspace,
+                 workspace_nbytes: int | None = None, stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check("dq_quant_report", lib().dq_quant_report(
+        ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), _ptr(prev_packed), _ptr(packed), _ptr(report),
+        _ptr(workspace), int(nbytes), _stream(stream)))
+
+
 def rescale_quantize_act(p: Problem, X, tokens: int, ldx: int, b, xq, x_scales, stream=None) -> None:
     _check("dq_rescale_quantize_act", lib().dq_rescale_quantize_act(
         ctypes.byref(p), _ptr(X), int(tokens), int(ldx), _ptr(b), _ptr(xq), _ptr(x_scales),
@@ -203,6 +213,13 @@ class Solver:
 
     def pack(self, stream=None):
         pack_codes(self.p, self.W, self.a, self.b, self.packed, stream)
+
+    def report(self, prev_packed=None, stream=None) -> torch.Tensor:
+        """Codes of the current state into ``packed`` plus a device tensor
+        [sum (W - a Q b)^2, sum W^2, codes differing from prev_packed]."""
+        out = torch.empty(3, dtype=torch.float64, device=self.W.device)
+        quant_report(self.p, self.W, self.a, self.b, prev_packed, self.packed, out, self.ws, stream=stream)
+        return out
 
     def solve(self, iters: int, stream=None):
         self.init(stream)

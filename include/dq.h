@@ -88,8 +88,9 @@ typedef struct {
   int32_t group, grid, a_fmt, b_fmt, w_type, reserved;
 } dq_problem;
 
-/* Bytes of device workspace dq_bcd_iterate and dq_init_colnorm need for
- * problem p (0 if p is invalid). Depends only on p's shape and format. */
+/* Bytes of device workspace dq_bcd_iterate, dq_init_colnorm and
+ * dq_quant_report need for problem p (0 if p is invalid). Depends only on
+ * p's shape and format. */
 size_t dq_workspace_bytes(const dq_problem* p);
 
 /* Absmax round-to-nearest initialization (DualQuant summary §3: symmetric
@@ -142,6 +143,25 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
  *                8-byte aligned; 8-bit grids: [rows, cols], 16-byte aligned */
 int dq_pack_codes(const dq_problem* p, const void* W, const void* a,
                   const uint16_t* b, uint8_t* packed, void* stream);
+
+/* Report on the state (a, b): its codes Q = q(W/(a b)) and
+ *   report[0] = sum (W - D_a Q D_b)^2        squared reconstruction error
+ *   report[1] = sum W^2                      (normalized error = [0] / [1])
+ *   report[2] = number of codes that differ from prev_packed (0 if NULL)
+ * as float64, summed in a fixed order (deterministic). These are the
+ * quantities the pages follow over the iterations (summary §5.3 and the
+ * convergence figure of App. B: normalized MSE and the share of codes that
+ * change); calling dq_bcd_iterate(1) and this in turn gives them per
+ * iteration, at the cost of one more read of W each.
+ *   prev_packed  in, may be NULL   codes of an earlier state, in
+ *                                  dq_pack_codes' layout and alignment
+ *   packed       out, may be NULL  this state's codes, as dq_pack_codes
+ *   report       out               3 float64 (device), 8-byte aligned
+ *   workspace    scratch of at least dq_workspace_bytes(p) bytes,
+ *                256-byte aligned */
+int dq_quant_report(const dq_problem* p, const void* W, const void* a, const uint16_t* b,
+                    const uint8_t* prev_packed, uint8_t* packed, double* report,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Activation side of the factorization X W^T ~= (X D_b) Q^T D_a (summary
  * §4.4: the column scale multiplies the activations inside the

@@ -107,6 +107,20 @@ def test_init_colnorm_checks_arguments_before_launch():
     assert L.dq_init_colnorm(ctypes.byref(p), ok, ok, ok, ctypes.c_void_p(128), need, None) == dq.ERR_WORKSPACE
 
 
+def test_quant_report_checks_arguments_before_launch():
+    L = dq.lib()
+    p = _p()
+    ok = ctypes.c_void_p(256)
+    need = L.dq_workspace_bytes(ctypes.byref(p))
+    assert L.dq_quant_report(ctypes.byref(p), ok, ok, ok, None, None, None, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_quant_report(ctypes.byref(p), ok, ok, ctypes.c_void_p(258), None, None, ok, ok, need,
+                             None) == dq.ERR_INVALID_ARG
+    assert L.dq_quant_report(ctypes.byref(p), ok, ok, ok, ctypes.c_void_p(260), None, ok, ok, need,
+                             None) == dq.ERR_INVALID_ARG
+    assert L.dq_quant_report(ctypes.byref(p), ok, ok, ok, None, None, ok, None, need, None) == dq.ERR_WORKSPACE
+    assert L.dq_quant_report(ctypes.byref(p), ok, ok, ok, None, None, ok, ok, need - 8, None) == dq.ERR_WORKSPACE
+
+
 def test_iterate_checks_workspace_and_stats_before_launch():
     L = dq.lib()
     p = _p()

@@ -194,6 +194,40 @@ def test_colnorm_init_then_iterate(name):
     assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
 
 
+# ------------------------------------------------------------ report
+
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxint8_g32", "mxfp8_g32"])
+def test_report_per_iteration_matches_oracle_history(name):
+    # dq_bcd_iterate(1) then dq_quant_report, in turn: the squared error of
+    # each iteration's state and the codes it changed, against the oracle's
+    # history (SSE after every sub-step; codes changed per iteration)
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    data = _mat(200, 384, 41)
+    T = 5
+    print(f"[case] report per iteration {name}", flush=True)
+    g = GpuRun(data, fmt)
+    g.s.init()
+    prev = torch.empty_like(g.s.packed)
+    r0 = g.s.report()
+    prev.copy_(g.s.packed)
+    got_sse, got_changed = [float(r0[0])], []
+    for _ in range(T):
+        g.s.iterate(1)
+        r = g.s.report(prev_packed=prev)
+        got_sse.append(float(r[0]))
+        got_changed.append(int(r[2]))
+        prev.copy_(g.s.packed)
+    torch.cuda.synchronize()
+    W64 = as_f64(data)
+    sol = D.solve(W64, ofmt, T, history=True)
+    want_sse = [sol.sse[0]] + [sol.sse[4 * (k + 1)] for k in range(T)]
+    np.testing.assert_allclose(got_sse, want_sse, rtol=1e-12)
+    assert got_changed == sol.changed
+    assert float(r[1]) == pytest.approx(float((W64 ** 2).sum()), rel=1e-12)
+    np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, ofmt))
+
+
 # ------------------------------------------------------------ state / determinism
 
 def test_iterations_compose_and_are_deterministic():
