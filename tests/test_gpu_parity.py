@@ -58,8 +58,9 @@ def test_every_format_ragged_shape(name, dtype):
     _check(data, fmt, 3, f"{name} {dtype} {M}x{N}")
 
 
-@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16"])
-@pytest.mark.parametrize("shape", [(1, 64), (2, 128), (64, 64), (65, 192), (300, 576)])
+@pytest.mark.parametrize("name", sorted(NAMED))
+@pytest.mark.parametrize("shape", [(1, 64), (2, 128), (64, 64), (65, 192), (300, 576), (3, 4096),
+                                   (2500, 64)])
 def test_named_formats_small_shapes(name, shape):
     fmt = NAMED[name]
     data = _mat(*shape, 11, "bf16", n_out=1)
@@ -75,8 +76,29 @@ def test_init_only(name):
 
 def test_padded_leading_dimension():
     data = _mat(100, 192, 5)
-    for name in ("int4_g64", "nvfp4_g16"):
+    for name in ("int4_g64", "nvfp4_g16", "mxint8_g32", "mxfp8_g32"):
         _check(data, NAMED[name], 3, f"{name} ldw 256", ldw=256)
+
+
+@pytest.mark.parametrize("name", sorted(NAMED))
+def test_all_zero_matrix(name):
+    # every slice is all-zero: every scale is 1 and every code 0
+    fmt = NAMED[name]
+    data = np.zeros((70, 128), dtype=np.uint16)
+    g = GpuRun(data, fmt).run(3)
+    assert np.all(g.a == 1.0) and np.all(g.b == 1.0) and np.all(g.Q == 0)
+    assert np.all(g.packed == 0)
+
+
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxint8_g32"])
+def test_rows_spanning_many_binades(name):
+    # row magnitudes from 2^-20 to 2^19: block scales of one column differ
+    # by up to 2^39, so the column sums mix widely different exponents
+    fmt = NAMED[name]
+    rng = np.random.default_rng(8)
+    W = rng.normal(0, 0.02, (160, 256)) * (2.0 ** (np.arange(160) % 40 - 20))[:, None]
+    data = synth.bf16_bits(W)
+    _check(data, fmt, 4, f"{name} rows over 40 binades")
 
 
 @pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32", "mxfp8_g32"])
