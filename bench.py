@@ -81,14 +81,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-COUNTERS_JSON = os.path.join(ROOT, "profiles", "bcd_pass_counters.json")
+def counters_json(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"bcd_pass_{workload}_counters.json")
 
 
 def recorded_traffic(workload: str):
     """Bytes moved per pass launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE measurement, or None if absent or taken on other sources."""
     try:
-        rec = json.load(open(COUNTERS_JSON))
+        rec = json.load(open(counters_json(workload)))
     except (OSError, ValueError):
         return None
     if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
@@ -100,7 +101,7 @@ def recorded_valu(workload: str):
     """VALU lane operations per pass launch from the committed rocprofv3
     SQ_INSTS_VALU measurement (wave instructions x 64), or None."""
     try:
-        rec = json.load(open(COUNTERS_JSON))
+        rec = json.load(open(counters_json(workload)))
     except (OSError, ValueError):
         return None
     if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:

@@ -10,7 +10,7 @@ Runs, each in its own rocprofv3 process:
      the two counters.
 and writes to OUT_DIR:
   bcd_pass_<workload>_kernel_trace.md   kernel-trace summary
-  bcd_pass_counters.json                traffic per pass launch + factors
+  bcd_pass_<workload>_counters.json     traffic per pass launch + factors
   bcd_pass_<workload>_counters.md       the same, readable
 
 Usage (on a machine with the GPU; rocprofv3 on PATH):
@@ -167,7 +167,7 @@ def main():
         "valu_lane_ops_per_element": 64.0 * sum(valu) / len(valu) / (M * N),
         "commands": {f"{k[0]}_{k[1]}": v for k, v in cmds.items()},
     }
-    json.dump(rec, open(os.path.join(args.out_dir, "bcd_pass_counters.json"), "w"), indent=2)
+    json.dump(rec, open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.json"), "w"), indent=2)
     md = [f"# HBM byte counters: bcd_pass_kernel, workload {wl.name}", "",
           f"Per pass launch (average of {len(pf)} dispatches): FETCH_SIZE {fetch_kib:.0f} KiB, "
           f"WRITE_SIZE {write_kib:.0f} KiB.", "",
