@@ -356,3 +356,32 @@ def test_llama_layer_set_on_streams():
             sol = D.solve(Ws, ofmt, 20)
             r = compare(Ws, a[:, s:s + 1], b[cs], Q[:, cs], sol, ofmt, f"{name} stripe {s}")
             assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, (name, s, r)
+
+
+def test_solve_captured_in_a_graph_replays_identically():
+    # every call only enqueues kernels on the caller's stream (no allocation,
+    # no memset, no host synchronization), so a whole solve can be captured
+    # in a HIP graph; replays with eager work in between must reproduce the
+    # eager result each time
+    fmt = NAMED["nvfp4_g16"]
+    data = _mat(256, 512, 51)
+    eager = GpuRun(data, fmt).run(5)
+    g = GpuRun(data, fmt)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            g.s.solve(5)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.s.a.zero_()
+        g.s.b.zero_()
+        g.s.packed.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(g.packed, eager.packed)
+        np.testing.assert_array_equal(g.s.a.cpu().numpy(), eager.s.a.cpu().numpy())
+        np.testing.assert_array_equal(g.s.b.cpu().numpy(), eager.s.b.cpu().numpy())
+        _ = (torch.ones(1024, device="cuda") * rep).sum().item()   # eager work between replays
