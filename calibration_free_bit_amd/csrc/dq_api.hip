@@ -212,6 +212,7 @@ int dq_rescale_quantize_act(const dq_problem* p, const void* X, int64_t tokens, 
   if (int s = check_problem(p)) return s;
   if (p->w_type != DQ_W_BF16) return DQ_ERR_UNSUPPORTED;  // X' = X D_b is exact only for bf16 X
   if (tokens < 0 || ldx < p->cols || (ldx * 2) % 16 != 0) return DQ_ERR_SHAPE;
+  if (tokens > (int64_t(1) << 40) / ldx) return DQ_ERR_SHAPE;  // keep offsets and grids in range
   if (tokens == 0) return DQ_OK;
   if (!X || !b || !xq || !x_scales || !aligned16(X) || !aligned16(b) || !aligned16(xq))
     return DQ_ERR_INVALID_ARG;

@@ -31,9 +31,14 @@ struct PassGeom {
 // Workspace: two alternating [n_tiles][max_seg][64][2] float64 buffers of
 // column partial sums.
 
-// Rows per chunk of the column-norm initialization's partial sums; its
-// workspace holds [n_tiles][ceil(M / kColnormRows)][64] float64.
+// Rows per chunk of the column-norm initialization's partial sums: 256, or
+// more when the chunk count would exceed the grid's y limit (65535). Its
+// workspace holds [n_tiles][chunks][64] float64, chunks <= ceil(M / 256).
 constexpr int kColnormRows = 256;
+inline int64_t colnorm_chunk_rows(int64_t M) {
+  const int64_t per = (M + 65534) / 65535;  // rows per chunk so that chunks <= 65535
+  return per <= kColnormRows ? kColnormRows : (per + 3) / 4 * 4;
+}
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,

@@ -73,18 +73,19 @@ __global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ 
 
 // ------------------------------------------- column-norm initialization
 
-// Partial column sums of |W| over chunks of kColnormRows rows: a workgroup
+// Partial column sums of |W| over chunks of chunk_rows rows: a workgroup
 // of 64 columns x 4 row-lanes per (tile, chunk); each lane adds every 4th
 // row of the chunk in order, then the 4 row-lanes are added pairwise.
 template <int WT>
 __global__ void __launch_bounds__(256) colnorm_partial_kernel(const void* __restrict__ W, int64_t ldw,
                                                               int64_t M, int64_t N,
+                                                              int64_t chunk_rows,
                                                               double* __restrict__ part) {
   __shared__ double s_sum[4][kTileCols];
   const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
   const int64_t tile = blockIdx.x, chunk = blockIdx.y;
   const int64_t j = tile * kTileCols + c;
-  const int64_t r0 = chunk * kColnormRows, r1 = min(r0 + kColnormRows, M);
+  const int64_t r0 = chunk * chunk_rows, r1 = min(r0 + chunk_rows, M);
   double acc = 0.0;
   if (j < N) {
     for (int64_t r = r0 + rl; r < r1; r += 4) {
@@ -707,8 +708,10 @@ template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                                double* part, hipStream_t st) {
   const int64_t n_tiles = (N + kTileCols - 1) / kTileCols;
-  const int64_t n_chunks = (M + kColnormRows - 1) / kColnormRows;
-  colnorm_partial_kernel<WT><<<dim3((unsigned)n_tiles, (unsigned)n_chunks), 256, 0, st>>>(W, ldw, M, N, part);
+  const int64_t chunk_rows = colnorm_chunk_rows(M);
+  const int64_t n_chunks = (M + chunk_rows - 1) / chunk_rows;
+  colnorm_partial_kernel<WT><<<dim3((unsigned)n_tiles, (unsigned)n_chunks), 256, 0, st>>>(
+      W, ldw, M, N, chunk_rows, part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   colnorm_b_kernel<<<(unsigned)n_tiles, kTileCols, 0, st>>>(part, n_chunks, M, N, b);
