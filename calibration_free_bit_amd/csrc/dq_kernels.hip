@@ -252,6 +252,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   AT* __restrict__ a = reinterpret_cast<AT*>(a_);
 
   int64_t f = (int64_t)blockIdx.x * g.L;
+  const int64_t f_first = f;
   const int64_t f_end = min(f + g.L, g.total);
   while (f < f_end) {
     const int64_t tile = (uint32_t)f / (uint32_t)g.S;
@@ -277,7 +278,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     for (int d = 0; d < kPrefetch; ++d)
       if (f + d < seg_end) issue(step + d, d);
 
-    __syncthreads();  // LDS of the previous segment is no longer read
+    if (f != f_first) __syncthreads();  // LDS of the previous segment is no longer read
     if (tid < kTileCols) {
       const int64_t j = tcol + tid;
       float bj = 1.0f;
