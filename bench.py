@@ -254,7 +254,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; "
-              "the solver shards by column stripes with no communication, see DESIGN.md",
+              "the solver shards by column stripes with no communication",
               file=sys.stderr)
         sys.exit(2)
 

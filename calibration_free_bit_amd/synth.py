@@ -11,7 +11,7 @@ or Student-t bodies with a few outlier input channels (columns), which is
 the structure that motivates the column scale ([DQ summary] §4.2; the
 outlier problem in [RTN tutorial] "When RTN Fails").
 
-Recipe (also stated in the design doc): ``numpy.random.default_rng(seed)``
+Recipe: ``numpy.random.default_rng(seed)``
 (PCG64); the body is drawn in float64 as one [M, N] array; then
 ``rng.choice(N, n_out, replace=False)`` picks n_out = round(frac * N) outlier
 columns, then their factors are drawn (a uniform range, or a constant);

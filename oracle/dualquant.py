@@ -25,7 +25,7 @@ copies (the ones that assign codes) are synchronized with the outer ones,
 and the codes are requantized after the row update and again after the
 column update. A slice whose codes are all zero gets scale 1.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 * one copy of each scale: synchronizing the inner copy right after each
   projection makes the two copies equal whenever codes are assigned;
 * a_i is per (row, block): the sums run over the G columns of the block;
@@ -139,7 +139,7 @@ def init_colnorm(W, fmt: Format):
 
     [DQ summary] §5.3: the starting point combines format-native row absmax
     scales with per-column L1-norm scales; the page gives no formula.
-    Reading (listed in the design doc): the column inverse scale is its column's
+    Reading: the column inverse scale is its column's
     mean absolute value projected onto F_b, b_j = Pi_Fb(sum_i |W_ij| / M)
     (1 for an all-zero column), and the block scales are the absmax
     initialization applied to W D_b^-1,

@@ -19,7 +19,7 @@ Sources
   [DQ repro] "Core equations": the projection acts on the inverse scales,
   since a scale format can store only some positive reals.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * integer rounding ties go to the even integer (``np.rint``);
 * E2M1 ties go to the level with the even encoding;
 * a scale is projected onto its format's legal positive values by nearest

@@ -1,7 +1,7 @@
-"""End-to-end check of the factorization the solver feeds (SURVEY next item:
-a W4A4 reference check; [DQ summary] §4.4 and App. I, [DQ repro] "Core
-equations": X W^T ~= (X D_b) Q^T D_a, with the column scale folded into the
-activation quantization and both operands in 4-bit codes with block scales).
+"""End-to-end check of the factorization the solver feeds, a W4A4 reference
+check ([DQ summary] §4.4 and App. I, [DQ repro] "Core equations":
+X W^T ~= (X D_b) Q^T D_a, with the column scale folded into the activation
+quantization and both operands in 4- or 8-bit codes with block scales).
 
 The library's outputs -- packed weight codes, block scales a and column
 scales b from the solver, packed activation codes and their scales from
