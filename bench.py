@@ -253,7 +253,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one GPU; "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark measures one GPU; "
               "the solver shards by column stripes with no communication",
               file=sys.stderr)
         sys.exit(2)
