@@ -44,7 +44,10 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 struct Workspace {
   PassGeom g;
-  size_t bytes;
+  size_t bytes;        // everything but dq_bcd_iterate with statistics
+  size_t pass_bytes;   // the two partial-sum buffers of the passes
+  size_t codes_bytes;  // one state's codes (statistics)
+  size_t stats_bytes;  // dq_bcd_iterate with statistics
 };
 
 Workspace pass_geometry(const dq_problem* p) {
@@ -69,8 +72,16 @@ Workspace pass_geometry(const dq_problem* p) {
   const size_t init_bytes = size_t(g.n_tiles) * size_t(ceil_div(p->rows, dq::kColnormRows)) *
                             dq::kTileCols * sizeof(double);
   // the report uses [workgroups][3] float64
-  const size_t report_bytes = size_t(dq::report_workgroups(p->rows, p->cols)) * 3 * sizeof(double);
+  const int64_t report_wg = dq::report_workgroups(p->rows, p->cols);
+  const size_t report_bytes = size_t(report_wg) * 3 * sizeof(double);
   w.bytes = align256(std::max({pass_bytes, init_bytes, report_bytes}));
+  // with statistics: the partials, then the codes of a state, then the
+  // per-workgroup sums of a pass or of the final report
+  const int code_bits = (p->grid == DQ_GRID_INT8 || p->grid == DQ_GRID_E4M3) ? 8 : 4;
+  w.pass_bytes = align256(pass_bytes);
+  w.codes_bytes = align256(size_t(p->rows) * size_t(p->cols) * code_bits / 8);
+  const size_t sums_bytes = align256(size_t(std::max(g.n_wg, report_wg)) * 3 * sizeof(double));
+  w.stats_bytes = std::max(w.bytes, w.pass_bytes + w.codes_bytes + sums_bytes);
   return w;
 }
 
@@ -134,6 +145,11 @@ size_t dq_workspace_bytes(const dq_problem* p) {
   return pass_geometry(p).bytes;
 }
 
+size_t dq_stats_workspace_bytes(const dq_problem* p) {
+  if (check_problem(p) != DQ_OK) return 0;
+  return pass_geometry(p).stats_bytes;
+}
+
 int dq_init_rtn(const dq_problem* p, const void* W, void* a, uint16_t* b, void* stream) {
   if (int s = check_problem(p)) return s;
   if (!W || !a || !b || !aligned16(W)) return DQ_ERR_INVALID_ARG;
@@ -161,15 +177,20 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
                    void* workspace, size_t workspace_bytes, double* stats, void* stream) {
   if (int s = check_problem(p)) return s;
   if (!W || !a || !b || !aligned16(W) || n_iters < 0) return DQ_ERR_INVALID_ARG;
-  if (stats) return DQ_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(stats) & 7u) return DQ_ERR_INVALID_ARG;
   if (n_iters == 0) return DQ_OK;
   const Workspace ws = pass_geometry(p);
-  if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  if (!workspace || workspace_bytes < (stats ? ws.stats_bytes : ws.bytes) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return DQ_ERR_WORKSPACE;
   double* part = static_cast<double*>(workspace);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  const dq::IterStats its{stats, base + ws.pass_bytes,
+                          reinterpret_cast<double*>(base + ws.pass_bytes + ws.codes_bytes)};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
-    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, st));
+    return hip_status(
+        dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, st));
   });
 }
 

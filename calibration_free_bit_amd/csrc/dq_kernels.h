@@ -60,9 +60,20 @@ template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_init(const void* W, int64_t ldw, int64_t M, int64_t N, void* a, uint16_t* b,
                        hipStream_t st);
 
+// Per-iteration statistics of dq_bcd_iterate: out [n_iters + 1][3] receives,
+// for the state after k iterations, sum (W - a Q b)^2, sum W^2 and the codes
+// changed since state k - 1 (0 for k = 0). codes holds [M][N * bits / 8]
+// state codes; part holds the per-workgroup sums (n_wg and the report
+// kernel's workgroups, 3 float64 each).
+struct IterStats {
+  double* out;
+  uint8_t* codes;
+  double* part;
+};
+
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, hipStream_t st);
+                          int n_iters, const IterStats* stats, hipStream_t st);
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,

@@ -219,11 +219,27 @@ __device__ __forceinline__ float column_scale(const double* __restrict__ part, c
 // One BCD iteration. b of the state comes from the partial column sums of
 // the previous pass (part_in) when there is one, else from b in memory;
 // this pass's partial column sums go to part_out.
-template <int WT, int GRID, int AFMT, int G>
+//
+// With STATS the pass also measures the state it starts from, (a, b) and its
+// codes Q: the float64 sums of (W - a Q b)^2 and W^2, and the number of
+// codes that differ from the codes in st.codes (the previous state's, when
+// st.has_prev), which it then overwrites with Q. Each thread sums its own
+// elements in order and the workgroup adds its threads in a fixed tree into
+// st.part[blockIdx.x][3], so the result does not depend on timing.
+struct PassStats {
+  uint8_t* codes;  // [M][N * bits / 8] codes of the previous state, then of this one
+  double* part;    // [n_wg][3] per-workgroup sums
+  int has_prev;
+};
+
+template <int WT, int GRID, int AFMT, int G, bool STATS>
 __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, const uint16_t* __restrict__ b,
-                    const double* __restrict__ part_in, double* __restrict__ part_out, PassGeom g) {
+                    const double* __restrict__ part_in, double* __restrict__ part_out, PassGeom g,
+                    PassStats st) {
   using AT = typename ScaleStore<AFMT>::T;
+  using Word = typename Grid<GRID>::Word;
+  constexpr int CB = Grid<GRID>::kBits;     // bits per stored code
   constexpr int LC = kLaneCols;             // contiguous columns per lane
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
   constexpr int RPW = 64 / LPR;             // rows per wave per step
@@ -250,6 +266,8 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   const int sub = lane % LPR, rl = lane / LPR;
   const int64_t nblk = g.N / G;
   AT* __restrict__ a = reinterpret_cast<AT*>(a_);
+  double st_sse = 0.0, st_w2 = 0.0;
+  int st_changed = 0;
 
   int64_t f = (int64_t)blockIdx.x * g.L;
   const int64_t f_first = f;
@@ -400,6 +418,29 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         }
         row_sums();
       }
+      if constexpr (STATS) {
+        // the state (a, b) this pass starts from, with its codes Q1
+        if (ok) {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+            for (int k = 0; k < BL; ++k) {
+              const int e = bl * BL + k;
+              // a Q b is exact in float64: q b is exact in float32
+              const double wk = (double)w[e];
+              const double d = wk - (double)(q[e] * LB(e)) * (double)a_old[bl];
+              st_sse = __builtin_fma(d, d, st_sse);
+              st_w2 = __builtin_fma(wk, wk, st_w2);
+            }
+          uint8_t* cp = st.codes + row * (g.N * CB / 8) + ccol * CB / 8;
+          const Word c0 = Grid<GRID>::encode8(q), c1 = Grid<GRID>::encode8(q + 8);
+          if (st.has_prev)
+            st_changed += Grid<GRID>::count_diff(c0, *reinterpret_cast<const Word*>(cp)) +
+                          Grid<GRID>::count_diff(c1, *reinterpret_cast<const Word*>(cp + CB));
+          *reinterpret_cast<Word*>(cp) = c0;
+          *reinterpret_cast<Word*>(cp + CB) = c1;
+        }
+      }
 #pragma unroll
       for (int m = 1; m < LPB; m <<= 1) {  // blocks wider than a lane
         num[0] += __shfl_xor(num[0], m);
@@ -497,7 +538,19 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       if (pi == 0) pw[c * 2 + qn] = acc;
       __syncthreads();
     }
+  }
 
+  if constexpr (STATS) {  // s_red is free: every segment ended with a barrier
+    s_red[tid] = st_sse;
+    s_red[kThreads + tid] = st_w2;
+    s_red[2 * kThreads + tid] = (double)st_changed;
+    __syncthreads();
+    for (int h = kThreads / 2; h > 0; h >>= 1) {
+      if (tid < h)
+        for (int i = 0; i < 3; ++i) s_red[i * kThreads + tid] += s_red[i * kThreads + tid + h];
+      __syncthreads();
+    }
+    if (tid < 3) st.part[(int64_t)blockIdx.x * 3 + tid] = s_red[tid * kThreads];
   }
 }
 
@@ -724,7 +777,7 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, hipStream_t st) {
+                          int n_iters, const IterStats* stats, hipStream_t st) {
   // partial buffers alternate between passes: pass k reads the partials of
   // pass k-1 (its column update) and writes its own to the other buffer
   const int64_t half = g.n_tiles * g.max_seg * kTileCols * 2;
@@ -732,12 +785,29 @@ hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, con
   for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
     const double* in = it == 0 ? nullptr : part + ((it - 1) & 1) * half;
     double* out = part + (it & 1) * half;
-    bcd_pass_kernel<WT, GRID, AFMT, G><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, in, out, g);
-    err = hipGetLastError();
+    if (!stats) {
+      bcd_pass_kernel<WT, GRID, AFMT, G, false><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
+          W, a, b, in, out, g, PassStats{});
+      err = hipGetLastError();
+    } else {
+      const PassStats ps{stats->codes, stats->part, it > 0 ? 1 : 0};
+      bcd_pass_kernel<WT, GRID, AFMT, G, true><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, in, out,
+                                                                                     g, ps);
+      err = hipGetLastError();
+      if (err == hipSuccess) {
+        report_reduce_kernel<<<1, 256, 0, st>>>(stats->part, g.n_wg, stats->out + 3 * it);
+        err = hipGetLastError();
+      }
+    }
   }
   if (err == hipSuccess && n_iters > 0) {
     bcd_column_kernel<<<(unsigned)g.n_tiles, kTileCols, 0, st>>>(part + ((n_iters - 1) & 1) * half, b, g);
     err = hipGetLastError();
+  }
+  if (err == hipSuccess && n_iters > 0 && stats) {
+    // the final state, against the codes the last pass left
+    err = launch_report<WT, GRID, AFMT, G>(W, g.ldw, g.M, g.N, a, b, stats->codes, nullptr,
+                                           stats->out + 3 * n_iters, stats->part, st);
   }
   return err;
 }
@@ -780,7 +850,8 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
   template hipError_t launch_init_colnorm<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, \
                                                          void*, uint16_t*, double*, hipStream_t); \
   template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
-                                                    const PassGeom&, int, hipStream_t);            \
+                                                    const PassGeom&, int, const IterStats*,        \
+                                                    hipStream_t);                                  \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
                                                  const void*, const uint16_t*, uint8_t*,          \
                                                  hipStream_t);                                    \

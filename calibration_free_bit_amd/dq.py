@@ -24,8 +24,9 @@ GRID_INT4, GRID_E2M1, GRID_INT8, GRID_E4M3 = 0, 1, 2, 3
 SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
-EXPORTS = ("dq_workspace_bytes", "dq_init_rtn", "dq_init_colnorm", "dq_bcd_iterate", "dq_pack_codes",
-           "dq_quant_report", "dq_rescale_quantize_act", "dq_status_string", "dq_abi_version")
+EXPORTS = ("dq_workspace_bytes", "dq_stats_workspace_bytes", "dq_init_rtn", "dq_init_colnorm",
+           "dq_bcd_iterate", "dq_pack_codes", "dq_quant_report", "dq_rescale_quantize_act",
+           "dq_status_string", "dq_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(Problem)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.dq_workspace_bytes.argtypes, L.dq_workspace_bytes.restype = [P], sz
+        L.dq_stats_workspace_bytes.argtypes, L.dq_stats_workspace_bytes.restype = [P], sz
         L.dq_init_rtn.argtypes, L.dq_init_rtn.restype = [P, vp, vp, vp, vp], ctypes.c_int
         L.dq_init_colnorm.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.dq_init_colnorm.restype = ctypes.c_int
@@ -134,6 +136,10 @@ def problem_for(W: torch.Tensor, fmt: Format) -> Problem:
 
 def workspace_bytes(p: Problem) -> int:
     return int(lib().dq_workspace_bytes(ctypes.byref(p)))
+
+
+def stats_workspace_bytes(p: Problem) -> int:
+    return int(lib().dq_stats_workspace_bytes(ctypes.byref(p)))
 
 
 def init_rtn(p: Problem, W, a, b, stream=None) -> None:
@@ -208,8 +214,19 @@ class Solver:
     def init_colnorm(self, stream=None):
         init_colnorm(self.p, self.W, self.a, self.b, self.ws, stream=stream)
 
-    def iterate(self, n: int, stream=None):
-        bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stream=stream)
+    def iterate(self, n: int, stream=None, stats: bool = False):
+        """n BCD iterations; with ``stats`` returns the device tensor
+        [n + 1, 3] of dq_bcd_iterate's per-iteration statistics (the larger
+        workspace they need is allocated on first use)."""
+        if not stats:
+            bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stream=stream)
+            return None
+        need = stats_workspace_bytes(self.p)
+        if self.ws.numel() < need:
+            self.ws = torch.empty((need,), dtype=torch.uint8, device=self.W.device)
+        out = torch.zeros((n + 1, 3), dtype=torch.float64, device=self.W.device)
+        bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stats=out, stream=stream)
+        return out
 
     def pack(self, stream=None):
         pack_codes(self.p, self.W, self.a, self.b, self.packed, stream)

@@ -93,6 +93,13 @@ typedef struct {
  * p's shape and format. */
 size_t dq_workspace_bytes(const dq_problem* p);
 
+/* Bytes of device workspace dq_bcd_iterate needs when it is given a stats
+ * array (0 if p is invalid): dq_workspace_bytes(p) plus room for one
+ * state's codes (rows x cols/2 bytes for 4-bit grids, rows x cols for
+ * 8-bit grids) and per-workgroup sums. A workspace of this size serves
+ * every call. */
+size_t dq_stats_workspace_bytes(const dq_problem* p);
+
 /* Absmax round-to-nearest initialization (DualQuant summary §3: symmetric
  * scale max|W| / qmax per block of G contiguous row elements; §5.3:
  * format-native row absmax scales). Writes a[i, g] = Pi_Fa(absmax / qmax)
@@ -128,10 +135,21 @@ int dq_init_colnorm(const dq_problem* p, const void* W, void* a, uint16_t* b,
  * n_iters = 0 is a no-op.
  *   W          in      [rows, ldw] of w_type
  *   a, b       in/out  as written by dq_init_rtn
- *   workspace  scratch of at least dq_workspace_bytes(p) bytes, 256-byte
- *              aligned; its contents are private to the call, and it must
- *              not be shared by calls that may run concurrently
- *   stats      must be NULL (reserved for per-iteration diagnostics) */
+ *   workspace  scratch of at least dq_workspace_bytes(p) bytes (with stats:
+ *              dq_stats_workspace_bytes(p)), 256-byte aligned; its contents
+ *              are private to the call, and it must not be shared by calls
+ *              that may run concurrently
+ *   stats      NULL, or out [n_iters + 1][3] float64 (device, 8-byte
+ *              aligned): row k describes the state after k iterations of
+ *              this call (row 0: the state passed in) with the quantities
+ *              of dq_quant_report -- sum (W - D_a Q D_b)^2, sum W^2 and the
+ *              number of codes that differ from those of state k - 1 (0 in
+ *              row 0). These are the convergence diagnostics the pages
+ *              follow (summary §5.3, App. B). Each pass measures the state
+ *              it starts from while it reads W, so rows 0 .. n_iters - 1
+ *              cost no extra read of W; row n_iters costs one. Sums run in
+ *              a fixed order (deterministic); a and b come out exactly as
+ *              without stats. */
 int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
                    int32_t n_iters, void* workspace, size_t workspace_bytes,
                    double* stats, void* stream);

@@ -244,6 +244,26 @@ def solve(W, fmt: Format, iters: int, a=None, b=None, history: bool = False) -> 
     return out
 
 
+def iteration_stats(W, fmt: Format, iters: int, a=None, b=None) -> np.ndarray:
+    """Convergence diagnostics of a solve, one row per state.
+
+    [DQ summary] §5.3 and the convergence figure of App. B follow the
+    normalized reconstruction error and the share of codes that change from
+    one iteration to the next. Row k (k = 0 .. iters) describes the state
+    after k iterations (row 0: the starting state): the squared
+    reconstruction error sum (W - D_a Q D_b)^2, sum W^2 (their ratio is the
+    normalized error) and the number of codes that differ from those of
+    state k - 1 (0 in row 0). Returns float64 [iters + 1, 3].
+    """
+    W = _check(W, fmt)
+    sol = solve(W, fmt, iters, a, b, history=True)
+    out = np.zeros((iters + 1, 3))
+    out[:, 0] = sol.sse[0::4]          # the start, then the end of every iteration
+    out[:, 1] = float((W * W).sum())
+    out[1:, 2] = sol.changed
+    return out
+
+
 # --------------------------------------------------------------------------
 # Emit: packed codes and native scale encodings
 # --------------------------------------------------------------------------

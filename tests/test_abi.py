@@ -50,6 +50,17 @@ def _p(**kw):
     return dq.Problem(**base)
 
 
+def test_stats_workspace_holds_one_state_of_codes():
+    L = dq.lib()
+    for grid, bits in ((dq.GRID_INT4, 4), (dq.GRID_E2M1, 4), (dq.GRID_INT8, 8), (dq.GRID_E4M3, 8)):
+        p = _p(rows=300, cols=576, ldw=576, grid=grid)
+        base = L.dq_workspace_bytes(ctypes.byref(p))
+        st = L.dq_stats_workspace_bytes(ctypes.byref(p))
+        assert st >= base + 300 * 576 * bits // 8
+    assert L.dq_stats_workspace_bytes(ctypes.byref(_p(cols=100))) == 0
+    assert L.dq_stats_workspace_bytes(None) == 0
+
+
 def test_workspace_bytes_valid_and_invalid():
     L = dq.lib()
     nb = L.dq_workspace_bytes(ctypes.byref(_p()))
@@ -130,7 +141,13 @@ def test_iterate_checks_workspace_and_stats_before_launch():
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, None, need, None, None) == dq.ERR_WORKSPACE
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ctypes.c_void_p(264), need, None,
                             None) == dq.ERR_WORKSPACE            # not 256-byte aligned
-    assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need, ok, None) == dq.ERR_UNSUPPORTED
+    # statistics need the larger workspace and an 8-byte aligned array
+    need_st = L.dq_stats_workspace_bytes(ctypes.byref(p))
+    assert need_st >= need and need_st % 256 == 0
+    assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need, ok, None) == dq.ERR_WORKSPACE
+    assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need_st - 1, ok, None) == dq.ERR_WORKSPACE
+    assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need_st, ctypes.c_void_p(260),
+                            None) == dq.ERR_INVALID_ARG
     # zero iterations is a no-op that touches nothing
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 0, None, 0, None, None) == dq.OK
 

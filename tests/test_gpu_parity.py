@@ -250,6 +250,60 @@ def test_report_per_iteration_matches_oracle_history(name):
     np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, ofmt))
 
 
+@pytest.mark.parametrize("name,shape,dtype", [
+    ("int4_g64", (200, 384), "bf16"), ("mxint4_g32", (197, 448), "bf16"), ("nvfp4_g16", (130, 208), "bf16"),
+    ("mxfp4_g32", (64, 256), "bf16"), ("mxint8_g32", (200, 384), "bf16"), ("mxfp8_g32", (129, 320), "bf16"),
+    ("int4_g64", (197, 256), "f32"), ("nvfp4_g16", (65, 144), "f32"),
+])
+def test_iterate_stats_match_oracle(name, shape, dtype):
+    # dq_bcd_iterate with a stats array: row k = (squared error, sum W^2,
+    # codes changed since state k - 1) of the state after k iterations
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    M, N = shape
+    data = _mat(M, N, 43, dtype)
+    T = 6
+    print(f"[case] iterate stats {name} {M}x{N} {dtype}", flush=True)
+    g = GpuRun(data, fmt)
+    g.s.init()
+    st = g.s.iterate(T, stats=True)
+    g.s.pack()
+    torch.cuda.synchronize()
+    got = st.cpu().numpy()
+    W64 = as_f64(data)
+    want = D.iteration_stats(W64, ofmt, T)
+    np.testing.assert_allclose(got[:, 0], want[:, 0], rtol=1e-11)
+    np.testing.assert_allclose(got[:, 1], want[:, 1], rtol=1e-12)
+    np.testing.assert_array_equal(got[:, 2], want[:, 2])
+    assert want[1:, 2].sum() > 0
+    # the statistics leave the solve untouched
+    plain = GpuRun(data, fmt).run(T)
+    np.testing.assert_array_equal(g.s.a.cpu().numpy(), plain.s.a.cpu().numpy())
+    np.testing.assert_array_equal(g.s.b.cpu().numpy(), plain.s.b.cpu().numpy())
+    np.testing.assert_array_equal(g.packed, plain.packed)
+
+
+def test_iterate_stats_across_calls():
+    # a second call starts from the state the first left: its row 0 is the
+    # first call's last row with no changed codes, and together they are
+    # the rows of one longer call
+    data = _mat(256, 512, 44)
+    fmt = NAMED["int4_g64"]
+    print("[case] iterate stats across calls", flush=True)
+    g = GpuRun(data, fmt)
+    g.s.init()
+    s1 = g.s.iterate(3, stats=True).cpu().numpy()
+    s2 = g.s.iterate(4, stats=True).cpu().numpy()
+    h = GpuRun(data, fmt)
+    h.s.init()
+    s7 = h.s.iterate(7, stats=True).cpu().numpy()
+    assert s2[0, 2] == 0
+    np.testing.assert_allclose(s2[0, :2], s1[3, :2], rtol=1e-12)
+    np.testing.assert_allclose(s7[:4], s1, rtol=1e-12)
+    np.testing.assert_allclose(s7[4:, :2], s2[1:, :2], rtol=1e-12)
+    np.testing.assert_array_equal(s7[4:, 2], s2[1:, 2])
+
+
 # ------------------------------------------------------------ state / determinism
 
 def test_iterations_compose_and_are_deterministic():

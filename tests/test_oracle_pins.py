@@ -13,6 +13,7 @@ requantization after each update, scale 1 where a slice has only zero codes);
 """
 
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -247,6 +248,32 @@ def test_sse_non_increasing_at_every_substep(fmt, seed):
     d = np.diff(s.sse)
     assert np.all(d <= 1e-12 * s.sse[0]), d.max()
     assert s.sse[-1] < s.sse[0]
+
+
+@pytest.mark.parametrize("fmt", [D.INT4_G64, D.NVFP4_G16, D.MXINT8_G32])
+def test_iteration_stats_recount_every_state(fmt):
+    # each row against a separate solve of k iterations: the squared error
+    # summed element by element, sum W^2, and the codes that differ from
+    # state k - 1 counted one by one
+    W = _w(8, 128, 5)
+    M, N = W.shape
+    T = 4
+    st = D.iteration_stats(W, fmt, T)
+    assert st.shape == (T + 1, 3)
+    w2 = math.fsum(float(x) * float(x) for x in W.ravel())
+    G = fmt.group
+    prev_Q = None
+    for k in range(T + 1):
+        s = D.solve(W, fmt, k)
+        err = math.fsum((W[i, j] - s.a[i, j // G] * s.Q[i, j] * s.b[j]) ** 2
+                        for i in range(M) for j in range(N))
+        assert st[k, 0] == pytest.approx(err, rel=1e-12)
+        assert st[k, 1] == pytest.approx(w2, rel=1e-14)
+        n_changed = 0 if prev_Q is None else sum(int(prev_Q[i, j] != s.Q[i, j])
+                                                 for i in range(M) for j in range(N))
+        assert st[k, 2] == n_changed
+        prev_Q = s.Q
+    assert np.all(np.diff(st[:, 0]) <= 1e-12 * st[0, 0])  # every sub-step is a block minimizer
 
 
 @pytest.mark.parametrize("fmt", FMTS)
