@@ -238,10 +238,32 @@ class Solver:
         quant_report(self.p, self.W, self.a, self.b, prev_packed, self.packed, out, self.ws, stream=stream)
         return out
 
-    def solve(self, iters: int, stream=None):
+    def solve(self, iters: int = 15, stream=None):
+        """init, ``iters`` iterations (15 by default, the count the DualQuant
+        summary §5.3 uses), pack."""
         self.init(stream)
         self.iterate(iters, stream)
         self.pack(stream)
+
+    def solve_until_stable(self, max_iters: int = 15, stream=None) -> int:
+        """init, then iterations one at a time until one changes no code
+        (the convergence criterion the summary §5.3 and App. B follow) or
+        ``max_iters`` have run; then pack. Returns the iterations run. The
+        state after k iterations is the one iterate(k) gives; each step
+        reads its changed-code count back to the host."""
+        if isinstance(stream, int):
+            raise ValueError("solve_until_stable needs a torch stream (or None)")
+        waiter = stream if stream is not None else torch.cuda.current_stream()
+        self.init(stream)
+        done = 0
+        while done < max_iters:
+            st = self.iterate(1, stream, stats=True)
+            done += 1
+            waiter.synchronize()
+            if int(st[1, 2].item()) == 0:
+                break
+        self.pack(stream)
+        return done
 
 
 def assign_streams(sizes, n_streams: int):

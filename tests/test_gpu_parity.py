@@ -304,6 +304,37 @@ def test_iterate_stats_across_calls():
     np.testing.assert_array_equal(s7[4:, 2], s2[1:, 2])
 
 
+@pytest.mark.parametrize("M,N,name,seed", [(16, 128, "int4_g64", 0), (16, 64, "nvfp4_g16", 3),
+                                            (24, 192, "mxint4_g32", 3)])
+def test_solve_until_stable_stops_where_the_oracle_does(M, N, name, seed):
+    # small matrices whose codes stop changing within 40 iterations
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    data = _mat(M, N, seed)
+    print(f"[case] solve until stable {name} {M}x{N} seed {seed}", flush=True)
+    g = GpuRun(data, fmt)
+    done = g.s.solve_until_stable(40)
+    torch.cuda.synchronize()
+    W64 = as_f64(data)
+    changed = D.iteration_stats(W64, ofmt, 40)[1:, 2]
+    assert (changed == 0).any()
+    assert done == int(np.nonzero(changed == 0)[0][0]) + 1
+    r = compare(W64, g.a, g.b, g.Q, D.solve(W64, ofmt, done), ofmt, f"until stable {name}")
+    assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}
+
+
+def test_solve_until_stable_caps_the_iterations():
+    data = _mat(64, 256, 0)
+    fmt = NAMED["int4_g64"]
+    print("[case] solve until stable, capped", flush=True)
+    g = GpuRun(data, fmt)
+    assert g.s.solve_until_stable(5) == 5
+    torch.cuda.synchronize()
+    plain = GpuRun(data, fmt).run(5)
+    np.testing.assert_array_equal(g.packed, plain.packed)
+    np.testing.assert_array_equal(g.s.a.cpu().numpy(), plain.s.a.cpu().numpy())
+
+
 # ------------------------------------------------------------ state / determinism
 
 def test_iterations_compose_and_are_deterministic():
