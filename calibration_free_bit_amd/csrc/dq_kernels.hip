@@ -695,11 +695,17 @@ static __global__ void __launch_bounds__(256) report_reduce_kernel(const double*
 
 // ------------------------------------------------------- activation side
 
-// One lane per 8 consecutive channels of a token (one 16-byte load of X and
-// of b), G/8 lanes per block: X' = X D_b (exact in float32 for bf16 X),
-// block absmax by lane shuffles, s = Pi(absmax / qmax), codes from the
-// float32 estimate X' * (1/s) with the exact re-decision of a wave that has
-// an element near a rounding midpoint.
+// One lane per 8 consecutive channels of kActTokens consecutive tokens (one
+// 16-byte load of X per token, one of b), G/8 lanes per block: X' = X D_b
+// (exact in float32 for bf16 X), block absmax by lane shuffles,
+// s = Pi(absmax / qmax), codes from the float32 estimate X' * (1/s) with the
+// exact re-decision of a wave that has an element near a rounding midpoint.
+// All loads are issued before any arithmetic, and b is converted once for
+// the lane's tokens. The projection of absmax / qmax takes the certified
+// float32 path of the pass kernel and falls back to float64 for a wave
+// with a quotient near a rounding boundary of the scale format.
+constexpr int kActTokens = 4;
+
 template <int GRID, int AFMT, int G>
 __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                         int64_t T, int64_t N,
@@ -708,39 +714,57 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
                                                         void* __restrict__ xs_) {
   using AT = typename ScaleStore<AFMT>::T;
   constexpr int LPB = G / 8;  // lanes per block; a block never straddles a wave
+  constexpr int B = Grid<GRID>::kBits;
   const int64_t nch = N / 8;
+  const int64_t n_tg = (T + kActTokens - 1) / kActTokens;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool live = idx < T * nch;
+  const bool live = idx < n_tg * nch;
   const int64_t cidx = live ? idx : 0;  // dead lanes compute on chunk 0
-  const int64_t t = cidx / nch, col = (cidx - t * nch) * 8;
-  const uint4 xv = *reinterpret_cast<const uint4*>(X + t * ldx + col);
+  const int64_t tg = cidx / nch, col = (cidx - tg * nch) * 8;
+  uint4 xv[kActTokens];
+#pragma unroll
+  for (int u = 0; u < kActTokens; ++u) {
+    const int64_t t = min(tg * kActTokens + u, T - 1);  // tokens past T read the last one
+    xv[u] = *reinterpret_cast<const uint4*>(X + t * ldx + col);
+  }
   const uint4 bv = *reinterpret_cast<const uint4*>(b + col);
-  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-  float x[8];
-  float amax = 0.0f;
+  const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+  float bf[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float xk = (k & 1) ? bf16_hi(xw[k >> 1]) : bf16_lo(xw[k >> 1]);
-    x[k] = xk * fp16_bits_to_float((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));  // exact product
-    amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
-  }
+  for (int k = 0; k < 8; ++k) bf[k] = fp16_bits_to_float((uint16_t)(bw[k >> 1] >> (16 * (k & 1))));
 #pragma unroll
-  for (int m = 1; m < LPB; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m));
-  const double s = amax > 0.0f ? project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0;
-  const float sf = (float)s, rs = __builtin_amdgcn_rcpf(sf);
-  float y[8], q[8];
+  for (int u = 0; u < kActTokens; ++u) {
+    const int64_t t = tg * kActTokens + u;
+    const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+    float x[8];
+    float amax = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
-  uint32_t diff[2];
-  if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
+    for (int k = 0; k < 8; ++k) {
+      const float xk = (k & 1) ? bf16_hi(xw[k >> 1]) : bf16_lo(xw[k >> 1]);
+      x[k] = xk * bf[k];  // exact product
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
-  }
-  if (live) {
-    constexpr int B = Grid<GRID>::kBits;
-    Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
-    if ((threadIdx.x % LPB) == 0) reinterpret_cast<AT*>(xs_)[t * (N / G) + col / G] = encode_scale<AFMT>(s);
+    for (int m = 1; m < LPB; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m));
+    bool unsure = false;
+    float sf = ls_scale_fast<AFMT>((double)amax, (double)Grid<GRID>::qmax, unsure);
+    if (wave_any(unsure))
+      sf = amax > 0.0f ? (float)project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0f;
+    const float rs = __builtin_amdgcn_rcpf(sf);
+    float y[8], q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
+    uint32_t diff[2];
+    if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
+    }
+    if (live && t < T) {
+      Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
+      if ((threadIdx.x % LPB) == 0)
+        reinterpret_cast<AT*>(xs_)[t * (N / G) + col / G] = encode_scale<AFMT>((double)sf);
+    }
   }
 }
 
@@ -837,8 +861,9 @@ hipError_t launch_report(const void* W, int64_t ldw, int64_t M, int64_t N, const
 template <int GRID, int AFMT, int G>
 hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, const uint16_t* b,
                       uint8_t* xq, void* xs, hipStream_t st) {
-  act_quant_kernel<GRID, AFMT, G><<<blocks_for(T * (N / 8), 256), 256, 0, st>>>(X, ldx, T, N, b, xq,
-                                                                              xs);
+  const int64_t n_tg = (T + kActTokens - 1) / kActTokens;
+  act_quant_kernel<GRID, AFMT, G><<<blocks_for(n_tg * (N / 8), 256), 256, 0, st>>>(X, ldx, T, N, b, xq,
+                                                                                 xs);
   return hipGetLastError();
 }
 
