@@ -177,3 +177,21 @@ def test_e4m3_element_ties_away_from_zero_is_caught(monkeypatch):
         return np.where(x < 0, -mag, mag) + 0.0
     monkeypatch.setattr(F, "round_e4m3", bad)
     assert _fails((TF.test_e4m3_elements_match_brute_force_and_torch, {}))
+
+
+@pytest.mark.parametrize("bug", ["shifted_state", "changed_off_by_one"])
+def test_iteration_stats_misaligned_rows_are_caught(monkeypatch, bug):
+    # a row taken one sub-step early, or the changed counts shifted by one
+    # iteration: the per-state recount must notice
+    orig = D.iteration_stats
+
+    def bad(W, fmt, iters, a=None, b=None):
+        st = orig(W, fmt, iters, a, b)
+        if bug == "shifted_state":
+            sol = D.solve(W, fmt, iters, a, b, history=True)
+            st[1:, 0] = sol.sse[3::4]        # after the column update, before requantizing
+        else:
+            st[1:-1, 2] = st[2:, 2]
+        return st
+    monkeypatch.setattr(D, "iteration_stats", bad)
+    assert _fails((TP.test_iteration_stats_recount_every_state, {"fmt": D.INT4_G64}))
