@@ -32,6 +32,9 @@ def common_flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # no packed-fp32 instructions anywhere in the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the first 14 dwords of kernel arguments arrive in SGPRs at wave
+        # launch instead of through a scalar load (gfx950 kernarg preload)
+        "-mllvm", "-amdgpu-kernarg-preload-count=14",
         "-I", INCLUDE, "-I", CSRC,
     ]
 

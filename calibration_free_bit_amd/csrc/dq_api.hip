@@ -32,6 +32,8 @@ int check_problem(const dq_problem* p) {
   if (p->b_fmt != DQ_SCALE_FP16) return DQ_ERR_UNSUPPORTED;
   if (p->w_type != DQ_W_F32 && p->w_type != DQ_W_BF16) return DQ_ERR_UNSUPPORTED;
   if (p->rows < 1 || p->cols < 1 || p->cols % p->group != 0) return DQ_ERR_SHAPE;
+  // the pass kernel takes its geometry as 32-bit kernel arguments
+  if (p->rows >= (int64_t(1) << 31) || p->ldw >= (int64_t(1) << 31)) return DQ_ERR_SHAPE;
   if (p->ldw < p->cols || (p->ldw * elem_size(p->w_type)) % 16 != 0) return DQ_ERR_SHAPE;
   if (p->rows > (int64_t(1) << 40) / p->ldw) return DQ_ERR_SHAPE;  // keep offsets far from overflow
   // the pass kernel's tile/step bookkeeping is 32-bit

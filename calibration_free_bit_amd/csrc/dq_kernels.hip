@@ -234,9 +234,15 @@ struct PassStats {
 
 template <int WT, int GRID, int AFMT, int G, bool STATS>
 __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
-    bcd_pass_kernel(const void* __restrict__ W, void* __restrict__ a_, const uint16_t* __restrict__ b,
-                    const double* __restrict__ part_in, double* __restrict__ part_out, PassGeom g,
-                    PassStats st) {
+    bcd_pass_kernel(const void* __restrict__ W, const double* __restrict__ part_in, void* __restrict__ a_,
+                    int32_t gM, int32_t gN, int32_t gldw, int32_t gS, int32_t gL, int32_t gtotal,
+                    int32_t gn_tiles, int32_t gmax_seg, const uint16_t* __restrict__ b,
+                    double* __restrict__ part_out, PassStats st) {
+  // the geometry comes as 32-bit scalars so that it arrives in preloaded
+  // kernel-argument registers
+  PassGeom g;
+  g.M = gM; g.N = gN; g.ldw = gldw; g.S = gS; g.L = gL; g.total = gtotal;
+  g.n_tiles = gn_tiles; g.max_seg = gmax_seg; g.n_wg = 0;
   using AT = typename ScaleStore<AFMT>::T;
   using Word = typename Grid<GRID>::Word;
   constexpr int CB = Grid<GRID>::kBits;     // bits per stored code
@@ -811,12 +817,14 @@ hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, con
     double* out = part + (it & 1) * half;
     if (!stats) {
       bcd_pass_kernel<WT, GRID, AFMT, G, false><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
-          W, a, b, in, out, g, PassStats{});
+          W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
+          (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, PassStats{});
       err = hipGetLastError();
     } else {
       const PassStats ps{stats->codes, stats->part, it > 0 ? 1 : 0};
-      bcd_pass_kernel<WT, GRID, AFMT, G, true><<<(unsigned)g.n_wg, kThreads, 0, st>>>(W, a, b, in, out,
-                                                                                     g, ps);
+      bcd_pass_kernel<WT, GRID, AFMT, G, true><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
+          W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
+          (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps);
       err = hipGetLastError();
       if (err == hipSuccess) {
         report_reduce_kernel<<<1, 256, 0, st>>>(stats->part, g.n_wg, stats->out + 3 * it);

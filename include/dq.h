@@ -72,8 +72,8 @@ typedef enum { DQ_SCALE_FP16 = 0, DQ_SCALE_E8M0 = 1, DQ_SCALE_E4M3 = 2 } dq_scal
 typedef enum { DQ_W_F32 = 0, DQ_W_BF16 = 1 } dq_wtype;
 
 /* One quantization problem. Fields are int32/int64 for a stable ABI.
- *   rows, cols  W is rows x cols (rows >= 1, cols >= G)
- *   ldw         row pitch of W (and of X) in elements, >= cols
+ *   rows, cols  W is rows x cols (1 <= rows < 2^31, cols >= G)
+ *   ldw         row pitch of W (and of X) in elements, cols <= ldw < 2^31
  *   group       G in {16, 32, 64}: block size along each row
  *   grid        dq_grid of the element codes
  *   a_fmt       dq_scale_fmt of the block scales

@@ -78,6 +78,8 @@ def test_workspace_bytes_valid_and_invalid():
     (dict(cols=100), dq.ERR_SHAPE),
     (dict(rows=0), dq.ERR_SHAPE),
     (dict(ldw=132), dq.ERR_SHAPE),             # 132 * 2 bytes is not a multiple of 16
+    (dict(ldw=1 << 31), dq.ERR_SHAPE),         # geometry is passed as 32-bit arguments
+    (dict(rows=1 << 31, ldw=128), dq.ERR_SHAPE),
     (dict(group=128), dq.ERR_UNSUPPORTED),
     (dict(grid=7), dq.ERR_UNSUPPORTED),
     (dict(a_fmt=9), dq.ERR_UNSUPPORTED),
