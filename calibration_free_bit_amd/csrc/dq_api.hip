@@ -192,7 +192,31 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
     return hip_status(
-        dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, st));
+        dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, false, st));
+  });
+}
+
+int dq_solve(const dq_problem* p, const void* W, void* a, uint16_t* b, int32_t n_iters,
+             uint8_t* packed, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int s = check_problem(p)) return s;
+  const bool byte_codes = p->grid == DQ_GRID_INT8 || p->grid == DQ_GRID_E4M3;
+  if (!W || !a || !b || !packed || !aligned16(W) || !aligned16(b) || n_iters < 0 ||
+      (reinterpret_cast<uintptr_t>(packed) & (byte_codes ? 15u : 7u)))
+    return DQ_ERR_INVALID_ARG;
+  const Workspace ws = pass_geometry(p);
+  if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DQ_ERR_WORKSPACE;
+  double* part = static_cast<double*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    hipError_t e = hipSuccess;
+    if (n_iters == 0)
+      e = dq::launch_init<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, st);
+    else
+      e = dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, true, st);
+    if (e == hipSuccess)
+      e = dq::launch_pack<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, packed, st);
+    return hip_status(e);
   });
 }
 

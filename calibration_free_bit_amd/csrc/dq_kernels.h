@@ -71,9 +71,12 @@ struct IterStats {
   double* part;
 };
 
+// n_iters BCD passes and the final column update; with from_init (and no
+// stats) the first pass starts from the absmax initialization it forms
+// itself, so a and b need not hold a state on entry.
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, const IterStats* stats, hipStream_t st);
+                          int n_iters, const IterStats* stats, bool from_init, hipStream_t st);
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,

@@ -232,7 +232,14 @@ struct PassStats {
   int has_prev;
 };
 
-template <int WT, int GRID, int AFMT, int G, bool STATS>
+// Pass variants: a plain iteration; one that also measures its starting
+// state (above); and the first iteration of a whole solve, which starts
+// from the absmax initialization (a = Pi_Fa(absmax / qmax) per block, 1 for
+// a zero block; b = 1) formed from the rows it reads instead of from a and
+// b in memory.
+enum : int { kPassPlain = 0, kPassStats = 1, kPassInit = 2 };
+
+template <int WT, int GRID, int AFMT, int G, int MODE>
 __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     bcd_pass_kernel(const void* __restrict__ W, const double* __restrict__ part_in, void* __restrict__ a_,
                     int32_t gM, int32_t gN, int32_t gldw, int32_t gS, int32_t gL, int32_t gtotal,
@@ -245,6 +252,8 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   g.n_tiles = gn_tiles; g.max_seg = gmax_seg; g.n_wg = 0;
   using AT = typename ScaleStore<AFMT>::T;
   using Word = typename Grid<GRID>::Word;
+  constexpr bool STATS = MODE == kPassStats;
+  constexpr bool INIT = MODE == kPassInit;
   constexpr int CB = Grid<GRID>::kBits;     // bits per stored code
   constexpr int LC = kLaneCols;             // contiguous columns per lane
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
@@ -294,8 +303,10 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     auto issue = [&](int64_t st, int slot) {
       const int64_t r = min(st * RPS + wave * RPW + rl, g.M - 1);
       raw[slot].load(W, r * g.ldw + ccol);
+      if constexpr (!INIT) {
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[r * nblk + (ccol + bl * BL) / G];
+        for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[r * nblk + (ccol + bl * BL) / G];
+      }
     };
     int64_t step = f - tile * g.S;
 #pragma unroll
@@ -306,7 +317,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     if (tid < kTileCols) {
       const int64_t j = tcol + tid;
       float bj = 1.0f;
-      if (j < g.N) bj = part_in ? column_scale(part_in, g, tile, tid) : fp16_bits_to_float(b[j]);
+      if (j < g.N && !INIT) bj = part_in ? column_scale(part_in, g, tile, tid) : fp16_bits_to_float(b[j]);
       s_b[tid] = bj;
       s_rb[tid] = 1.0f / bj;
     }
@@ -348,8 +359,34 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       float w[LC];
       raw[SLOT].unpack(w);
       float a_old[NB];
+      if constexpr (INIT) {
+        // the absmax start, from this row's block (shuffles join the lanes
+        // of a block wider than a lane); certified float32 projection
+        float amax[NB];
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) a_old[bl] = decode_scale<AFMT>(a_raw[SLOT][bl]);
+        for (int bl = 0; bl < NB; ++bl) {
+          amax[bl] = 0.0f;
+#pragma unroll
+          for (int k = 0; k < BL; ++k) amax[bl] = __builtin_fmaxf(amax[bl], __builtin_fabsf(w[bl * BL + k]));
+        }
+#pragma unroll
+        for (int m = 1; m < LPB; m <<= 1) amax[0] = __builtin_fmaxf(amax[0], __shfl_xor(amax[0], m));
+        bool unsure = false;
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl)
+          a_old[bl] = amax[bl] > 0.0f ? ls_scale_fast<AFMT>((double)amax[bl], (double)Grid<GRID>::qmax, unsure)
+                                      : 1.0f;
+        if (wave_any(unsure)) {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl)
+            a_old[bl] = amax[bl] > 0.0f
+                            ? (float)project<AFMT>((double)amax[bl] / (double)Grid<GRID>::qmax)
+                            : 1.0f;
+        }
+      } else {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) a_old[bl] = decode_scale<AFMT>(a_raw[SLOT][bl]);
+      }
       const bool ok = row_ok && lane_cols_ok;
       if (!full) {
 #pragma unroll
@@ -361,8 +398,10 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       if (f + kPrefetch < seg_end) {
         if ((step + kPrefetch + 1) * RPS <= g.M) {  // that step is entirely inside M
           raw[SLOT].load(wp + kPrefetch * wstep, 0);
+          if constexpr (!INIT) {
 #pragma unroll
-          for (int bl = 0; bl < NB; ++bl) a_raw[SLOT][bl] = a[ai + kPrefetch * astep + bl * BL / G];
+            for (int bl = 0; bl < NB; ++bl) a_raw[SLOT][bl] = a[ai + kPrefetch * astep + bl * BL / G];
+          }
         } else {
           issue(step + kPrefetch, SLOT);
         }
@@ -805,9 +844,21 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
   return hipGetLastError();
 }
 
+template <int WT, int GRID, int AFMT, int G, int MODE>
+hipError_t launch_pass(const void* W, const double* in, void* a, uint16_t* b, double* out,
+                       const PassGeom& g, const PassStats& ps, hipStream_t st) {
+  bcd_pass_kernel<WT, GRID, AFMT, G, MODE><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
+      W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
+      (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps);
+  return hipGetLastError();
+}
+
+// n_iters passes from the state (a, b) -- or, with from_init, from the
+// absmax initialization, which the first pass forms itself -- then the
+// final column update into b.
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, const IterStats* stats, hipStream_t st) {
+                          int n_iters, const IterStats* stats, bool from_init, hipStream_t st) {
   // partial buffers alternate between passes: pass k reads the partials of
   // pass k-1 (its column update) and writes its own to the other buffer
   const int64_t half = g.n_tiles * g.max_seg * kTileCols * 2;
@@ -815,21 +866,17 @@ hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, con
   for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
     const double* in = it == 0 ? nullptr : part + ((it - 1) & 1) * half;
     double* out = part + (it & 1) * half;
-    if (!stats) {
-      bcd_pass_kernel<WT, GRID, AFMT, G, false><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
-          W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
-          (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, PassStats{});
-      err = hipGetLastError();
-    } else {
+    if (stats) {
       const PassStats ps{stats->codes, stats->part, it > 0 ? 1 : 0};
-      bcd_pass_kernel<WT, GRID, AFMT, G, true><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
-          W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
-          (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps);
-      err = hipGetLastError();
+      err = launch_pass<WT, GRID, AFMT, G, kPassStats>(W, in, a, b, out, g, ps, st);
       if (err == hipSuccess) {
         report_reduce_kernel<<<1, 256, 0, st>>>(stats->part, g.n_wg, stats->out + 3 * it);
         err = hipGetLastError();
       }
+    } else if (it == 0 && from_init) {
+      err = launch_pass<WT, GRID, AFMT, G, kPassInit>(W, in, a, b, out, g, PassStats{}, st);
+    } else {
+      err = launch_pass<WT, GRID, AFMT, G, kPassPlain>(W, in, a, b, out, g, PassStats{}, st);
     }
   }
   if (err == hipSuccess && n_iters > 0) {
@@ -883,7 +930,7 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
   template hipError_t launch_init_colnorm<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t, \
                                                          void*, uint16_t*, double*, hipStream_t); \
   template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
-                                                    const PassGeom&, int, const IterStats*,        \
+                                                    const PassGeom&, int, const IterStats*, bool,  \
                                                     hipStream_t);                                  \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
                                                  const void*, const uint16_t*, uint8_t*,          \

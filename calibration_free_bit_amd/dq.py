@@ -25,7 +25,7 @@ SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
 EXPORTS = ("dq_workspace_bytes", "dq_stats_workspace_bytes", "dq_init_rtn", "dq_init_colnorm",
-           "dq_bcd_iterate", "dq_pack_codes", "dq_quant_report", "dq_rescale_quantize_act",
+           "dq_bcd_iterate", "dq_solve", "dq_pack_codes", "dq_quant_report", "dq_rescale_quantize_act",
            "dq_status_string", "dq_abi_version")
 
 
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         L.dq_init_colnorm.restype = ctypes.c_int
         L.dq_bcd_iterate.argtypes = [P, vp, vp, vp, i32, vp, sz, vp, vp]
         L.dq_bcd_iterate.restype = ctypes.c_int
+        L.dq_solve.argtypes, L.dq_solve.restype = [P, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int
         L.dq_pack_codes.argtypes, L.dq_pack_codes.restype = [P, vp, vp, vp, vp, vp], ctypes.c_int
         L.dq_quant_report.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dq_quant_report.restype = ctypes.c_int
@@ -159,6 +160,14 @@ def bcd_iterate(p: Problem, W, a, b, n_iters: int, workspace, workspace_nbytes: 
     _check("dq_bcd_iterate", lib().dq_bcd_iterate(
         ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), int(n_iters), _ptr(workspace), int(nbytes),
         _ptr(stats), _stream(stream)))
+
+
+def solve(p: Problem, W, a, b, n_iters: int, packed, workspace, workspace_nbytes: int | None = None,
+          stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace_nbytes is None else workspace_nbytes
+    _check("dq_solve", lib().dq_solve(
+        ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), int(n_iters), _ptr(packed), _ptr(workspace), int(nbytes),
+        _stream(stream)))
 
 
 def pack_codes(p: Problem, W, a, b, packed, stream=None) -> None:
@@ -240,10 +249,9 @@ class Solver:
 
     def solve(self, iters: int = 15, stream=None):
         """init, ``iters`` iterations (15 by default, the count the DualQuant
-        summary §5.3 uses), pack."""
-        self.init(stream)
-        self.iterate(iters, stream)
-        self.pack(stream)
+        summary §5.3 uses), pack -- one dq_solve call, whose first pass
+        forms the initialization itself."""
+        solve(self.p, self.W, self.a, self.b, iters, self.packed, self.ws, stream=stream)
 
     def solve_until_stable(self, max_iters: int = 15, stream=None) -> int:
         """init, then iterations one at a time until one changes no code

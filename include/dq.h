@@ -154,6 +154,20 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
                    int32_t n_iters, void* workspace, size_t workspace_bytes,
                    double* stats, void* stream);
 
+/* The whole solve in one call: dq_init_rtn, dq_bcd_iterate(n_iters) and
+ * dq_pack_codes, with a, b and packed exactly as those three calls leave
+ * them. The absmax initialization is formed inside the first iteration's
+ * pass from the rows it reads, which saves one read of W and a launch;
+ * n_iters = 0 runs the initialization and the packing alone.
+ *   W          in   [rows, ldw] of w_type
+ *   a, b       out  the final state, encodings as for dq_init_rtn; b
+ *                   16-byte aligned
+ *   packed     out  as for dq_pack_codes
+ *   workspace  scratch of at least dq_workspace_bytes(p) bytes, 256-byte
+ *              aligned */
+int dq_solve(const dq_problem* p, const void* W, void* a, uint16_t* b, int32_t n_iters,
+             uint8_t* packed, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Final codes Q = q(W/(a b)), packed two per byte (summary App. I: packed
  * offline for deployment).
  *   b       in   [cols] fp16 bits, 16-byte aligned

@@ -154,6 +154,19 @@ def test_iterate_checks_workspace_and_stats_before_launch():
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 0, None, 0, None, None) == dq.OK
 
 
+def test_solve_checks_arguments_before_launch():
+    L = dq.lib()
+    p = _p()
+    ok = ctypes.c_void_p(256)
+    need = L.dq_workspace_bytes(ctypes.byref(p))
+    assert L.dq_solve(ctypes.byref(p), ok, ok, ok, 3, None, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_solve(ctypes.byref(p), ok, ok, ok, -1, ok, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_solve(ctypes.byref(p), ok, ok, ctypes.c_void_p(258), 3, ok, ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_solve(ctypes.byref(p), ok, ok, ok, 3, ctypes.c_void_p(260), ok, need, None) == dq.ERR_INVALID_ARG
+    assert L.dq_solve(ctypes.byref(p), ok, ok, ok, 3, ok, ok, need - 1, None) == dq.ERR_WORKSPACE
+    assert L.dq_solve(ctypes.byref(_p(cols=100)), ok, ok, ok, 3, ok, ok, need, None) == dq.ERR_SHAPE
+
+
 def test_activation_call_validation():
     L = dq.lib()
     p = _p()

@@ -174,6 +174,68 @@ def test_zero_slices():
         _check(data, fmt, 3, f"{name} zero slices")
 
 
+# ------------------------------------------------ whole solve in one call
+
+def _separate_calls(data, fmt, iters, ldw=None):
+    g = GpuRun(data, fmt, ldw)
+    g.s.init()
+    g.s.iterate(iters)
+    g.s.pack()
+    torch.cuda.synchronize()
+    return g
+
+
+def _one_call(data, fmt, iters, ldw=None):
+    g = GpuRun(data, fmt, ldw)
+    g.s.a.fill_(0x55)                  # nothing may be read from a or b
+    g.s.b.fill_(0x7BFF)
+    g.s.solve(iters)
+    torch.cuda.synchronize()
+    return g
+
+
+def _same_state(x, y):
+    np.testing.assert_array_equal(x.s.a.cpu().numpy(), y.s.a.cpu().numpy())
+    np.testing.assert_array_equal(x.s.b.cpu().numpy(), y.s.b.cpu().numpy())
+    np.testing.assert_array_equal(x.packed, y.packed)
+
+
+@pytest.mark.parametrize("name", sorted(ALL_FORMATS))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_solve_equals_init_iterate_pack(name, dtype):
+    # dq_solve forms the absmax start inside its first pass; the result must
+    # be the three separate calls' bit for bit, and the oracle's
+    fmt = ALL_FORMATS[name]
+    G = fmt.group
+    M, N = 197, 3 * 64 + (G if G < 64 else 0)
+    data = _mat(M, N, 8, dtype, std=1.0 if fmt.a_fmt == dq.SCALE_E4M3 else 0.02)
+    print(f"[case] solve {name} {dtype} {M}x{N}", flush=True)
+    one = _one_call(data, fmt, 3)
+    _same_state(one, _separate_calls(data, fmt, 3))
+    W64 = as_f64(data)
+    ofmt = oracle_fmt(fmt)
+    compare(W64, one.a, one.b, one.Q, D.solve(W64, ofmt, 3), ofmt, f"solve {name} {dtype}")
+
+
+@pytest.mark.parametrize("iters", [0, 1, 2])
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxint8_g32", "mxfp8_g32"])
+def test_solve_few_iterations_zero_slices_and_padding(name, iters):
+    data = _mat(130, 320, 9)
+    data[5, 64:128] = 0                # an all-zero block
+    data[:, 200] = 0                   # an all-zero column
+    data[7, :] = 0                     # an all-zero row
+    fmt = NAMED[name]
+    print(f"[case] solve {name} T={iters} zero slices, padded rows", flush=True)
+    _same_state(_one_call(data, fmt, iters, ldw=336), _separate_calls(data, fmt, iters, ldw=336))
+
+
+def test_solve_all_zero_matrix():
+    data = np.zeros((64, 128), dtype=np.uint16)
+    fmt = NAMED["nvfp4_g16"]
+    g = _one_call(data, fmt, 2)
+    assert np.all(g.a == 1.0) and np.all(g.b == 1.0) and not g.packed.any()
+
+
 # ------------------------------------------------ column-norm initialization
 
 def _colnorm_run(data, fmt, iters, ldw=None):
