@@ -19,12 +19,18 @@
 // the NEXT pass: each of its workgroups adds the partials of its tile in a
 // fixed order (the kernel boundary makes them visible; no fences or
 // atomics), and a small kernel writes b after the last pass. Partials
-// alternate between two buffers so a pass never overwrites what it reads. Q is never stored: it is recomputed from (W, a, b) whenever
-// needed, so one iteration reads W once.
+// alternate between two buffers so a pass never overwrites what it reads.
+// Q is never stored: it is recomputed from (W, a, b) whenever needed, so
+// one iteration reads W once. Two variants of the pass add work to the same
+// stream of rows: one measures the state it starts from (per-iteration
+// statistics), one forms the absmax initialization itself (the first pass
+// of a whole solve).
 //
 // Every sum of the least-squares updates is accumulated in float64 in a
-// fixed order: each product is exact and, for bf16 weights, every partial
-// sum is exact, so the result does not depend on the order at all.
+// fixed order, so results are deterministic. Each product is exact (at most
+// 26 significant bits), so a sum is exact as long as its terms span less
+// than about 2^(27 - log2 of their count) in magnitude, which holds for
+// ordinary weights; then the summation order does not matter at all.
 #include <hip/hip_runtime.h>
 
 #include <utility>
@@ -172,8 +178,8 @@ __device__ __forceinline__ uint32_t tile_n_seg(const PassGeom& g, uint32_t tile)
   return ((tile + 1) * (uint32_t)g.S - 1) / (uint32_t)g.L - tile_first_wg(g, tile) + 1;
 }
 
-// The loads are split from the sums so that a caller can issue the first
-// batch early and overlap its latency with other loads.
+// The partials of one column of a tile, loaded kBatch at a time (all in
+// flight together) and added in segment order.
 struct ColumnPartials {
   static constexpr int kBatch = 8;  // loads in flight
   const double2* pt;
@@ -220,7 +226,7 @@ __device__ __forceinline__ float column_scale(const double* __restrict__ part, c
 // the previous pass (part_in) when there is one, else from b in memory;
 // this pass's partial column sums go to part_out.
 //
-// With STATS the pass also measures the state it starts from, (a, b) and its
+// The kPassStats variant also measures the state it starts from, (a, b) and its
 // codes Q: the float64 sums of (W - a Q b)^2 and W^2, and the number of
 // codes that differ from the codes in st.codes (the previous state's, when
 // st.has_prev), which it then overwrites with Q. Each thread sums its own
