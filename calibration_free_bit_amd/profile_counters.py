@@ -69,12 +69,23 @@ def _find(root, suffix):
     raise FileNotFoundError(f"{suffix} under {root}")
 
 
+def _matches(kernel_name: str, name_has: str) -> bool:
+    """name_has in the kernel's name; for the pass kernel only its plain
+    instantiation (last template argument 0), not the first pass of a
+    whole solve or the statistics variant."""
+    if name_has not in kernel_name:
+        return False
+    if name_has == "bcd_pass_kernel":
+        return kernel_name.split(">(")[0].endswith(", 0")
+    return True
+
+
 def _counters(root, counter, name_has):
     """Per-dispatch values of one counter, for kernels whose name contains
     name_has (summed over the counter's dimensions)."""
     per = defaultdict(float)
     for r in csv.DictReader(open(_find(root, "counter_collection.csv"))):
-        if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]:
+        if r["Counter_Name"] == counter and _matches(r["Kernel_Name"], name_has):
             per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
     return [per[k] for k in sorted(per)]
 
@@ -94,7 +105,7 @@ def main():
     work = tempfile.mkdtemp(prefix="dqprof_", dir="/tmp")
 
     # 1. kernel trace
-    tr, tr_cmd = _rocprof(["--kernel-trace", "--stats"], bench_args + ["--steps", "5", "--warmup", "1"],
+    tr, tr_cmd = _rocprof(["--kernel-trace", "--stats"], bench_args,
                           "trace", work)
     stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
     lines = [f"# Kernel trace: BCD solver, workload {wl.name}", "",
