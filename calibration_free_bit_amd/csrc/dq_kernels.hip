@@ -51,6 +51,17 @@ __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
+// The value of lane (lane ^ M) within each quad of lanes (M = 1 or 2), by a
+// DPP quad permutation (VALU moves instead of an LDS round trip).
+template <int M>
+__device__ __forceinline__ double quad_xor(double v) {
+  static_assert(M == 1 || M == 2, "quad permutations");
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), kCtrl, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
 // ------------------------------------------------------------------ init
 
 // One thread per (row, block): absmax -> a = Pi(absmax / qmax), 1 if zero.
@@ -492,10 +503,15 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
           *reinterpret_cast<Word*>(cp + CB) = c1;
         }
       }
-#pragma unroll
-      for (int m = 1; m < LPB; m <<= 1) {  // blocks wider than a lane
-        num[0] += __shfl_xor(num[0], m);
-        den[0] += __shfl_xor(den[0], m);
+      // blocks wider than a lane: the lanes of a block form (part of) a quad
+      static_assert(LPB <= 4 && LPR == 4, "a block's lanes lie in one quad");
+      if constexpr (LPB >= 2) {
+        num[0] += quad_xor<1>(num[0]);
+        den[0] += quad_xor<1>(den[0]);
+      }
+      if constexpr (LPB >= 4) {
+        num[0] += quad_xor<2>(num[0]);
+        den[0] += quad_xor<2>(den[0]);
       }
 
       // project, synchronize the copy that assigns codes, store
@@ -584,8 +600,8 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       const int c = (cr % LPR) * LC + cr / LPR;  // the column of LDS row cr
 #pragma unroll 8
       for (int r = 0; r < RPS / 4; ++r) acc += s_red[cr * kRedStride + r * 4 + pi];
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
+      acc += quad_xor<1>(acc);
+      acc += quad_xor<2>(acc);
       if (pi == 0) pw[c * 2 + qn] = acc;
       __syncthreads();
     }
