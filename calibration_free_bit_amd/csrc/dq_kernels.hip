@@ -301,13 +301,17 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   double st_sse = 0.0, st_w2 = 0.0;
   int st_changed = 0;
 
-  int64_t f = (int64_t)blockIdx.x * g.L;
-  const int64_t f_first = f;
-  const int64_t f_end = min(f + g.L, g.total);
+  // Step bookkeeping in 32 bits (the host keeps S * n_tiles below 2^31 and
+  // rows below 2^31, so S * RPS + RPS fits in uint32): uniform counters stay
+  // in scalar registers and compare there.
+  const uint32_t S32 = (uint32_t)g.S, M32 = (uint32_t)g.M;
+  uint32_t f = blockIdx.x * (uint32_t)g.L;
+  const uint32_t f_first = f;
+  const uint32_t f_end = min(f + (uint32_t)g.L, (uint32_t)g.total);
   while (f < f_end) {
-    const int64_t tile = (uint32_t)f / (uint32_t)g.S;
-    const int64_t seg_end = min(f_end, (tile + 1) * g.S);
-    const int64_t tcol = tile * kTileCols;
+    const uint32_t tile = f / S32;
+    const uint32_t seg_end = min(f_end, (tile + 1) * S32);
+    const int64_t tcol = (int64_t)tile * kTileCols;
     const int64_t col0 = tcol + sub * LC;
     const bool lane_cols_ok = col0 < g.N;
     const int64_t ccol = lane_cols_ok ? col0 : 0;  // clamped column for loads
@@ -317,15 +321,15 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     // row M-1; out of range values are zeroed before use.
     RawRow<WT, LC> raw[kPrefetch];
     AT a_raw[kPrefetch][NB];
-    auto issue = [&](int64_t st, int slot) {
-      const int64_t r = min(st * RPS + wave * RPW + rl, g.M - 1);
+    auto issue = [&](uint32_t st, int slot) {
+      const int64_t r = min(st * RPS + wave * RPW + rl, M32 - 1);
       raw[slot].load(W, r * g.ldw + ccol);
       if constexpr (!INIT) {
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[r * nblk + (ccol + bl * BL) / G];
       }
     };
-    int64_t step = f - tile * g.S;
+    uint32_t step = f - tile * S32;
 #pragma unroll
     for (int d = 0; d < kPrefetch; ++d)
       if (f + d < seg_end) issue(step + d, d);
@@ -360,18 +364,18 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     // by one step of RPS rows at a time.
     const int64_t wstep = (int64_t)RPS * g.ldw * EB;
     const int64_t astep = (int64_t)RPS * nblk;
-    int64_t row = step * RPS + wave * RPW + rl;
-    const char* wp = reinterpret_cast<const char*>(W) + (row * g.ldw + ccol) * EB;
-    int64_t ai = row * nblk + ccol / G;
+    uint32_t row = step * RPS + wave * RPW + rl;
+    const char* wp = reinterpret_cast<const char*>(W) + ((int64_t)row * g.ldw + ccol) * EB;
+    int64_t ai = (int64_t)row * nblk + ccol / G;
 
     // One row step; the ring slot is a compile-time constant so that no
     // in-flight register is ever copied (the loop below is unrolled by
     // kPrefetch).
     auto row_step = [&]<int SLOT>() {
-      const bool row_ok = row < g.M;
+      const bool row_ok = row < M32;
       // rows past M occur only in the last step of a tile, columns past N
       // only in the last tile
-      const bool full = (step + 1) * RPS <= g.M && tcol + kTileCols <= g.N;
+      const bool full = (step + 1) * RPS <= M32 && tcol + kTileCols <= g.N;
 
       float w[LC];
       raw[SLOT].unpack(w);
@@ -413,7 +417,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       }
       // refill this slot with the step kPrefetch ahead
       if (f + kPrefetch < seg_end) {
-        if ((step + kPrefetch + 1) * RPS <= g.M) {  // that step is entirely inside M
+        if ((step + kPrefetch + 1) * RPS <= M32) {  // that step is entirely inside M
           raw[SLOT].load(wp + kPrefetch * wstep, 0);
           if constexpr (!INIT) {
 #pragma unroll
@@ -586,7 +590,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
     run_slots(std::make_integer_sequence<int, kPrefetch>{});
 
     // ---- reduce the RPS row-lanes of each column, write this segment's partial
-    const int64_t seg = (int64_t)blockIdx.x - tile_first_wg(g, (uint32_t)tile);
+    const int64_t seg = (int64_t)blockIdx.x - tile_first_wg(g, tile);
     double* __restrict__ pw = part_out + (tile * g.max_seg + seg) * (kTileCols * 2);
 #pragma unroll
     for (int qn = 0; qn < 2; ++qn) {
