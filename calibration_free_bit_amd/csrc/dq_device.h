@@ -121,10 +121,13 @@ __device__ __forceinline__ double ls_scale(double num, double den) {
 
 // Fast path of ls_scale, in float32. The quotient num/den is formed from
 // the float32 roundings of num and den and a 1-ulp reciprocal, so it is
-// within 5 * 2^-24 (relative) of the exact quotient; the projection of that
-// approximation is the projection of the exact quotient unless it lies
-// within kScaleSure (relative) of a rounding boundary of the scale format,
-// in which case `unsure` is set and the caller must use ls_scale.
+// within 5 * 2^-24 (relative) of the exact quotient. For fp16 and E4M3 the
+// hardware conversions (round to nearest even, subnormals kept) project
+// both ends of [x (1 - 2^-20), x (1 + 2^-20)], which contains the exact
+// (clamped) quotient; rounding is monotone, so equal results at both ends
+// are the projection of the exact quotient. For E8M0 the quotient is
+// compared with the nearest binade midpoint. Otherwise `unsure` is set and
+// the caller must use ls_scale.
 constexpr float kScaleSure = 0x1p-20f;
 
 template <int AFMT>
@@ -143,18 +146,19 @@ __device__ __forceinline__ float ls_scale_fast(double num, double den, bool& uns
     const float mid = __builtin_ldexpf(1.5f, k);
     unsure |= __builtin_fabsf(x - mid) <= kScaleSure * x;
     return __builtin_ldexpf(1.0f, min(x >= mid ? k + 1 : k, 127));
+  } else if constexpr (AFMT == kScaleFp16) {
+    const float x = __builtin_amdgcn_fmed3f(qf, 0x1p-24f, 65504.0f);
+    const _Float16 rl = (_Float16)(x * (1.0f - kScaleSure));
+    const _Float16 rh = (_Float16)(x * (1.0f + kScaleSure));
+    unsure |= __builtin_bit_cast(uint16_t, rl) != __builtin_bit_cast(uint16_t, rh);
+    return (float)rl;
   } else {
-    constexpr float lo = AFMT == kScaleFp16 ? 0x1p-24f : 0x1p-9f;
-    constexpr float hi = AFMT == kScaleFp16 ? 65504.0f : 448.0f;
-    constexpr int kmin = AFMT == kScaleFp16 ? -14 : -6;           // smallest normal binade
-    constexpr int mbits = AFMT == kScaleFp16 ? 10 : 3;            // fraction bits
-    const float x = __builtin_fminf(__builtin_fmaxf(qf, lo), hi);
-    const int k = max(__builtin_amdgcn_frexp_expf(x) - 1, kmin);
-    const float c = __builtin_ldexpf(1.5f, k - mbits + 23);      // ulp of x + c is 2^(k-mbits)
-    const float r = (x + c) - c;                                 // nearest, ties to even
-    const float h = __builtin_ldexpf(1.0f, k - mbits - 1);       // half a step
-    unsure |= h - __builtin_fabsf(x - r) <= kScaleSure * x;
-    return r;
+    // OCP E4M3FN conversion of both ends into bytes 0 and 1 (the upper end
+    // stays below 464, where the conversion would give NaN)
+    const float x = __builtin_amdgcn_fmed3f(qf, 0x1p-9f, 448.0f);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x * (1.0f - kScaleSure), x * (1.0f + kScaleSure), 0, false);
+    unsure |= ((w ^ (w >> 8)) & 0xFF) != 0;
+    return __builtin_amdgcn_cvt_f32_fp8(w, 0);
   }
 }
 
