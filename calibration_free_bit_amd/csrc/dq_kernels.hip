@@ -61,6 +61,12 @@ __device__ __forceinline__ double quad_xor(double v) {
   const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), kCtrl, 0xF, 0xF, false);
   return __hiloint2double(hi, lo);
 }
+template <int M>
+__device__ __forceinline__ float quad_xor(float v) {
+  static_assert(M == 1 || M == 2, "quad permutations");
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
 
 // ------------------------------------------------------------------ init
 
@@ -390,8 +396,8 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 #pragma unroll
           for (int k = 0; k < BL; ++k) amax[bl] = __builtin_fmaxf(amax[bl], __builtin_fabsf(w[bl * BL + k]));
         }
-#pragma unroll
-        for (int m = 1; m < LPB; m <<= 1) amax[0] = __builtin_fmaxf(amax[0], __shfl_xor(amax[0], m));
+        if constexpr (LPB >= 2) amax[0] = __builtin_fmaxf(amax[0], quad_xor<1>(amax[0]));
+        if constexpr (LPB >= 4) amax[0] = __builtin_fmaxf(amax[0], quad_xor<2>(amax[0]));
         bool unsure = false;
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
