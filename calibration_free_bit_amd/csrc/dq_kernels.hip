@@ -67,6 +67,11 @@ __device__ __forceinline__ float quad_xor(float v) {
   constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
+// The value of lane 7 - (lane & 7) within each group of 8 lanes (DPP
+// row_half_mirror): pairs every lane of one quad with one of the other.
+__device__ __forceinline__ float half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+}
 
 // ------------------------------------------------------------------ init
 
@@ -821,8 +826,10 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
       x[k] = xk * bf[k];  // exact product
       amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
     }
-#pragma unroll
-    for (int m = 1; m < LPB; m <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m));
+    static_assert(LPB <= 8, "a block's lanes lie in one group of 8");
+    if constexpr (LPB >= 2) amax = __builtin_fmaxf(amax, quad_xor<1>(amax));
+    if constexpr (LPB >= 4) amax = __builtin_fmaxf(amax, quad_xor<2>(amax));
+    if constexpr (LPB >= 8) amax = __builtin_fmaxf(amax, half_mirror(amax));
     bool unsure = false;
     float sf = ls_scale_fast<AFMT>((double)amax, (double)Grid<GRID>::qmax, unsure);
     if (wave_any(unsure))
