@@ -46,7 +46,7 @@ def decode_b(b_t: torch.Tensor) -> np.ndarray:
     return F.decode_scale(b_t.cpu().numpy().view(np.uint16), "fp16")
 
 
-class GpuRun:
+class DeviceRun:
     """One matrix on the GPU: init, iterate, pack through the C ABI."""
 
     def __init__(self, data: np.ndarray, fmt: dq.Format, ldw: int | None = None):

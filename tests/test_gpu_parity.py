@@ -16,7 +16,7 @@ import torch
 
 from calibration_free_bit_amd import dq, synth
 from oracle import dualquant as D
-from tests.gpu_util import ALL_FORMATS, GpuRun, as_f64, compare, oracle_fmt
+from tests.gpu_util import ALL_FORMATS, DeviceRun, as_f64, compare, oracle_fmt
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _mat(M, N, seed, dtype="bf16", std=0.02, n_out=3, fac=20.0):
 
 def _check(data, fmt, iters, what, ldw=None):
     print(f"[case] {what}", flush=True)
-    g = GpuRun(data, fmt, ldw).run(iters)
+    g = DeviceRun(data, fmt, ldw).run(iters)
     W64 = as_f64(data)
     sol = D.solve(W64, oracle_fmt(fmt), iters)
     return compare(W64, g.a, g.b, g.Q, sol, oracle_fmt(fmt), what)
@@ -85,7 +85,7 @@ def test_all_zero_matrix(name):
     # every slice is all-zero: every scale is 1 and every code 0
     fmt = NAMED[name]
     data = np.zeros((70, 128), dtype=np.uint16)
-    g = GpuRun(data, fmt).run(3)
+    g = DeviceRun(data, fmt).run(3)
     assert np.all(g.a == 1.0) and np.all(g.b == 1.0) and np.all(g.Q == 0)
     assert np.all(g.packed == 0)
 
@@ -108,7 +108,7 @@ def test_exact_ties_power_of_two_scales(name):
     # decides them on both sides.
     data = _mat(256, 256, 9, n_out=0)
     fmt = NAMED[name]
-    g = GpuRun(data, fmt).run(0)
+    g = DeviceRun(data, fmt).run(0)
     W64 = as_f64(data)
     sol = D.solve(W64, oracle_fmt(fmt), 0)
     ties = D.code_ties(W64, sol.a, sol.b, oracle_fmt(fmt))
@@ -124,7 +124,7 @@ def test_exact_ties_e2m1_power_of_two_scales():
     # ties go to the even encoding on both sides.
     data = _mat(256, 256, 9, n_out=0)
     fmt = NAMED["mxfp4_g32"]
-    g = GpuRun(data, fmt).run(0)
+    g = DeviceRun(data, fmt).run(0)
     W64 = as_f64(data)
     sol = D.solve(W64, oracle_fmt(fmt), 0)
     ties = D.code_ties(W64, sol.a, sol.b, oracle_fmt(fmt))
@@ -168,7 +168,7 @@ def test_zero_slices():
     data[:, 200] = 0                   # an all-zero column
     for name in ("int4_g64", "nvfp4_g16"):
         fmt = NAMED[name]
-        g = GpuRun(data, fmt).run(3)
+        g = DeviceRun(data, fmt).run(3)
         assert np.all(g.b[200] == 1.0)
         assert np.all(g.a[5, 64 // fmt.group:128 // fmt.group] == 1.0)
         _check(data, fmt, 3, f"{name} zero slices")
@@ -177,7 +177,7 @@ def test_zero_slices():
 # ------------------------------------------------ whole solve in one call
 
 def _separate_calls(data, fmt, iters, ldw=None):
-    g = GpuRun(data, fmt, ldw)
+    g = DeviceRun(data, fmt, ldw)
     g.s.init()
     g.s.iterate(iters)
     g.s.pack()
@@ -186,7 +186,7 @@ def _separate_calls(data, fmt, iters, ldw=None):
 
 
 def _one_call(data, fmt, iters, ldw=None):
-    g = GpuRun(data, fmt, ldw)
+    g = DeviceRun(data, fmt, ldw)
     g.s.a.fill_(0x55)                  # nothing may be read from a or b
     g.s.b.fill_(0x7BFF)
     g.s.solve(iters)
@@ -239,7 +239,7 @@ def test_solve_all_zero_matrix():
 # ------------------------------------------------ column-norm initialization
 
 def _colnorm_run(data, fmt, iters, ldw=None):
-    g = GpuRun(data, fmt, ldw)
+    g = DeviceRun(data, fmt, ldw)
     g.s.init_colnorm()
     if iters:
         g.s.iterate(iters)
@@ -290,7 +290,7 @@ def test_report_per_iteration_matches_oracle_history(name):
     data = _mat(200, 384, 41)
     T = 5
     print(f"[case] report per iteration {name}", flush=True)
-    g = GpuRun(data, fmt)
+    g = DeviceRun(data, fmt)
     g.s.init()
     prev = torch.empty_like(g.s.packed)
     r0 = g.s.report()
@@ -326,7 +326,7 @@ def test_iterate_stats_match_oracle(name, shape, dtype):
     data = _mat(M, N, 43, dtype)
     T = 6
     print(f"[case] iterate stats {name} {M}x{N} {dtype}", flush=True)
-    g = GpuRun(data, fmt)
+    g = DeviceRun(data, fmt)
     g.s.init()
     st = g.s.iterate(T, stats=True)
     g.s.pack()
@@ -339,7 +339,7 @@ def test_iterate_stats_match_oracle(name, shape, dtype):
     np.testing.assert_array_equal(got[:, 2], want[:, 2])
     assert want[1:, 2].sum() > 0
     # the statistics leave the solve untouched
-    plain = GpuRun(data, fmt).run(T)
+    plain = DeviceRun(data, fmt).run(T)
     np.testing.assert_array_equal(g.s.a.cpu().numpy(), plain.s.a.cpu().numpy())
     np.testing.assert_array_equal(g.s.b.cpu().numpy(), plain.s.b.cpu().numpy())
     np.testing.assert_array_equal(g.packed, plain.packed)
@@ -352,11 +352,11 @@ def test_iterate_stats_across_calls():
     data = _mat(256, 512, 44)
     fmt = NAMED["int4_g64"]
     print("[case] iterate stats across calls", flush=True)
-    g = GpuRun(data, fmt)
+    g = DeviceRun(data, fmt)
     g.s.init()
     s1 = g.s.iterate(3, stats=True).cpu().numpy()
     s2 = g.s.iterate(4, stats=True).cpu().numpy()
-    h = GpuRun(data, fmt)
+    h = DeviceRun(data, fmt)
     h.s.init()
     s7 = h.s.iterate(7, stats=True).cpu().numpy()
     assert s2[0, 2] == 0
@@ -374,7 +374,7 @@ def test_solve_until_stable_stops_where_the_oracle_does(M, N, name, seed):
     ofmt = oracle_fmt(fmt)
     data = _mat(M, N, seed)
     print(f"[case] solve until stable {name} {M}x{N} seed {seed}", flush=True)
-    g = GpuRun(data, fmt)
+    g = DeviceRun(data, fmt)
     done = g.s.solve_until_stable(40)
     torch.cuda.synchronize()
     W64 = as_f64(data)
@@ -389,10 +389,10 @@ def test_solve_until_stable_caps_the_iterations():
     data = _mat(64, 256, 0)
     fmt = NAMED["int4_g64"]
     print("[case] solve until stable, capped", flush=True)
-    g = GpuRun(data, fmt)
+    g = DeviceRun(data, fmt)
     assert g.s.solve_until_stable(5) == 5
     torch.cuda.synchronize()
-    plain = GpuRun(data, fmt).run(5)
+    plain = DeviceRun(data, fmt).run(5)
     np.testing.assert_array_equal(g.packed, plain.packed)
     np.testing.assert_array_equal(g.s.a.cpu().numpy(), plain.s.a.cpu().numpy())
 
@@ -402,12 +402,12 @@ def test_solve_until_stable_caps_the_iterations():
 def test_iterations_compose_and_are_deterministic():
     data = _mat(384, 512, 13)
     fmt = NAMED["int4_g64"]
-    g7 = GpuRun(data, fmt).run(7)
-    g34 = GpuRun(data, fmt).run(3)
+    g7 = DeviceRun(data, fmt).run(7)
+    g34 = DeviceRun(data, fmt).run(3)
     g34.run(4, init=False)
     for x, y in ((g7.a, g34.a), (g7.b, g34.b), (g7.packed, g34.packed)):
         np.testing.assert_array_equal(x, y)
-    again = GpuRun(data, fmt).run(7)
+    again = DeviceRun(data, fmt).run(7)
     np.testing.assert_array_equal(again.packed, g7.packed)
     np.testing.assert_array_equal(again.s.a.cpu().numpy(), g7.s.a.cpu().numpy())
 
@@ -418,7 +418,7 @@ def test_iterations_compose_and_are_deterministic():
 def test_packed_bytes_equal_oracle_packing(name):
     fmt = NAMED[name]
     data = _mat(96, 256, 21)
-    g = GpuRun(data, fmt).run(2)
+    g = DeviceRun(data, fmt).run(2)
     sol = D.solve(as_f64(data), oracle_fmt(fmt), 2)
     np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, oracle_fmt(fmt)))
 
@@ -431,7 +431,7 @@ def test_activation_rescale_quantize(name, tokens):
     ofmt = oracle_fmt(fmt)
     N = 512
     data = _mat(64, N, 23)
-    g = GpuRun(data, fmt).run(2)                       # b from a real solve
+    g = DeviceRun(data, fmt).run(2)                       # b from a real solve
     X = synth.make_activations(tokens, N, 29)
     Xd = torch.from_numpy(X.view(np.int16)).cuda()
     xq = torch.empty((tokens, N * fmt.code_bits // 8), dtype=torch.uint8, device="cuda")
@@ -458,7 +458,7 @@ def test_full_size_sampled_stripes(wl_name):
     ofmt = oracle_fmt(fmt)
     m = synth.make_matrix(wl.spec, wl.seeds[0])
     print(f"[case] {wl_name} full solve T={wl.iters}", flush=True)
-    g = GpuRun(m.data, fmt).run(wl.iters)
+    g = DeviceRun(m.data, fmt).run(wl.iters)
     a, b, Q = g.a, g.b, g.Q
     G = fmt.group
     n_str = m.spec.cols // G
@@ -490,7 +490,7 @@ def test_llama_layer_set_on_streams():
     G = fmt.group
     mats = [synth.make_matrix(spec, seed) for (_, _, _, spec, seed) in items]
     print("[case] llama layer 0 on 4 streams, T=20", flush=True)
-    runs = [GpuRun(m.data, fmt) for m in mats]
+    runs = [DeviceRun(m.data, fmt) for m in mats]
     streams = [torch.cuda.Stream() for _ in range(4)]
     dq.solve_on_streams([r.s for r in runs], 20, streams)
     torch.cuda.synchronize()
@@ -512,8 +512,8 @@ def test_solve_captured_in_a_graph_replays_identically():
     # eager result each time
     fmt = NAMED["nvfp4_g16"]
     data = _mat(256, 512, 51)
-    eager = GpuRun(data, fmt).run(5)
-    g = GpuRun(data, fmt)
+    eager = DeviceRun(data, fmt).run(5)
+    g = DeviceRun(data, fmt)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
