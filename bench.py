@@ -87,8 +87,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def profile_stem(workload: str) -> str:
+    """File stem of a workload's rocprofv3 summaries in profiles/: the
+    profiled kernel, then the workload."""
+    if workload.startswith("act_"):
+        return "act_quant_" + workload[len("act_"):]
+    return f"bcd_pass_{workload}"
+
+
 def counters_json(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"bcd_pass_{workload}_counters.json")
+    return os.path.join(ROOT, "profiles", f"{profile_stem(workload)}_counters.json")
 
 
 def recorded_traffic(workload: str):
@@ -272,9 +280,19 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from calibration_free_bit_amd import synth as _synth
+    known = [SET_WORKLOAD, *_synth.WORKLOADS, *_synth.ACT_WORKLOADS]
+    if args.workload not in known:
+        print(f"bench.py: unknown workload {args.workload!r}; one of: {', '.join(known)}",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload == SET_WORKLOAD:
         _step_counts(args, steps=10, warmup=2)
         run_set(args)
+        return
+    if args.workload.startswith("act_"):
+        _step_counts(args, steps=100, warmup=200)
+        run_act(args)
         return
     _step_counts(args, steps=100, warmup=200)
 
@@ -363,6 +381,99 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data)
+    print(json.dumps(out))
+
+
+def act_bytes_per_elem(code_bits: int, a_bytes: int, G: int, tokens: int) -> float:
+    """One read of X (bf16), the codes and the per-token block scales
+    written, the column scales read (2 bytes, amortized over the tokens)."""
+    return 2.0 + code_bits / 8.0 + a_bytes / G + 2.0 / tokens
+
+
+def act_cpu_baseline(aw, X, bbits, budget_s: float = 10.0):
+    """The float64 oracle on a prefix of the tokens, repeated for about
+    budget_s seconds."""
+    from calibration_free_bit_amd import synth
+    from oracle import dualquant as D
+
+    fmt = D.FORMATS[aw.fmt]
+    b = bbits.view("float16").astype("float64")
+    k = min(aw.tokens, 256)
+    Xs = synth.bf16_to_f64(X[:k])
+    reps, dt = 0, 0.0
+    t0 = time.perf_counter()
+    while reps == 0 or dt < budget_s:
+        D.rescale_quantize_act(Xs, b, fmt)
+        reps += 1
+        dt = time.perf_counter() - t0
+    return {"value": Xs.size * reps / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle, the first {k} of {aw.tokens} tokens "
+                      f"({k}x{aw.cols}), {reps} run(s) in {dt:.1f} s"}
+
+
+def run_act(args):
+    """Activation quantization with the column scales folded in
+    (dq_rescale_quantize_act): one step quantizes the whole token batch."""
+    import numpy as np
+    import torch
+
+    from calibration_free_bit_amd import dq, synth
+
+    aw = synth.ACT_WORKLOADS[args.workload]
+    fmt = dq.FORMATS[aw.fmt]
+    X = synth.make_activations(aw.tokens, aw.cols, aw.seed)
+    bbits = synth.make_col_scales(aw.cols, aw.seed + 1)
+    Xd = torch.from_numpy(X.view(np.int16)).to("cuda:0")
+    bd = torch.from_numpy(bbits.view(np.int16)).to("cuda:0")
+    xq = torch.empty((aw.tokens, aw.cols * fmt.code_bits // 8), dtype=torch.uint8, device="cuda:0")
+    xs = torch.empty((aw.tokens, aw.cols // fmt.group), dtype=fmt.a_dtype, device="cuda:0")
+    p = dq.problem(1, aw.cols, fmt, dq.W_BF16, aw.cols)
+    st = torch.cuda.current_stream()
+
+    def step():
+        dq.rescale_quantize_act(p, Xd, aw.tokens, aw.cols, bd, xq, xs, st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e_start.record(st)
+    for _ in range(args.steps):
+        step()
+    e_end.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e_start.elapsed_time(e_end) / args.steps
+    elems = aw.tokens * aw.cols
+    a_bytes = 2 if fmt.a_fmt == dq.SCALE_FP16 else 1
+    b_alg = act_bytes_per_elem(fmt.code_bits, a_bytes, fmt.group, aw.tokens)
+    # one kernel per step, launched back to back: the step time is the
+    # launch time
+    achieved = b_alg * elems / (step_ms * 1e-3) / 1e9
+    out = {
+        "metric": "activation elements/s",
+        "value": elems / (step_ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32",
+        "data": "synthetic (seeded, numpy PCG64)",
+        "config": {"workload": aw.name, "tokens": aw.tokens, "cols": aw.cols, "format": aw.fmt,
+                   "group": fmt.group, "seed": aw.seed, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(aw.name),
+                     "kernel": "act_quant_kernel", "alg_bytes_per_elem": b_alg,
+                     "avg_launch_us": step_ms * 1e3},
+        "breakdown_ms": {"wall_per_step": wall * 1e3 / args.steps},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = act_cpu_baseline(aw, X, bbits)
     print(json.dumps(out))
 
 

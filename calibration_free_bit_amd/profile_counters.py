@@ -4,14 +4,16 @@ Runs, each in its own rocprofv3 process:
   1. --kernel-trace --stats of ``bench.py`` (per-kernel average durations);
   2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of ``bench.py`` (HBM bytes per
      dispatch, in KiB), then --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_WAVES
-     (instructions issued by the pass kernel);
+     (instructions issued by the profiled kernel: the BCD pass for a weight
+     workload, the activation quantizer for an ``act_`` workload);
   3. the same two counters for ``bench.py --copy-calibration``, a plain
      device copy of 256 MiB, whose known bytes give the scale factors of
      the two counters.
-and writes to OUT_DIR:
-  bcd_pass_<workload>_kernel_trace.md   kernel-trace summary
-  bcd_pass_<workload>_counters.json     traffic per pass launch + factors
-  bcd_pass_<workload>_counters.md       the same, readable
+and writes to OUT_DIR (STEM: bcd_pass_<workload>, or act_quant_<...> for
+an activation workload act_<...>):
+  STEM_kernel_trace.md   kernel-trace summary
+  STEM_counters.json     traffic per launch + factors
+  STEM_counters.md       the same, readable
 
 Usage (on a machine with the GPU; rocprofv3 on PATH):
   python -m calibration_free_bit_amd.profile_counters OUT_DIR [--workload W]
@@ -100,15 +102,33 @@ def main():
     import bench  # for the source hash and the workload definition
     from calibration_free_bit_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    bench_args = [BENCH, "--workload", wl.name, "--no-cpu-baseline"]
+    from calibration_free_bit_amd import dq
+    if args.workload in synth.ACT_WORKLOADS:
+        aw = synth.ACT_WORKLOADS[args.workload]
+        kernel, what = "act_quant_kernel", "activation quantization"
+        launch, unit = "launch", "activation element"
+        M, N = aw.tokens, aw.cols
+        fmt = dq.FORMATS[aw.fmt]
+        b_alg = bench.act_bytes_per_elem(fmt.code_bits, 2 if fmt.a_fmt == dq.SCALE_FP16 else 1,
+                                         fmt.group, M)
+    else:
+        wl = synth.WORKLOADS[args.workload]
+        kernel, what = "bcd_pass_kernel", "BCD solver"
+        launch, unit = "pass launch", "weight element"
+        M, N = wl.spec.rows, wl.spec.cols
+        fmt = dq.FORMATS[wl.fmt]
+        b_alg = bench.alg_bytes_per_elem(2 if wl.spec.dtype == "bf16" else 4,
+                                         2 if fmt.a_fmt == dq.SCALE_FP16 else 1, fmt.group, M)
+    name = args.workload
+    stem = bench.profile_stem(name)
+    bench_args = [BENCH, "--workload", name, "--no-cpu-baseline"]
     work = tempfile.mkdtemp(prefix="dqprof_", dir="/tmp")
 
     # 1. kernel trace
     tr, tr_cmd = _rocprof(["--kernel-trace", "--stats"], bench_args,
                           "trace", work)
     stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
-    lines = [f"# Kernel trace: BCD solver, workload {wl.name}", "",
+    lines = [f"# Kernel trace: {what}, workload {name}", "",
              "Command:", "", f"    {tr_cmd}", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |",
              "|---|---:|---:|---:|---:|---:|"]
@@ -116,7 +136,7 @@ def main():
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} % |")
-    open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_kernel_trace.md"), "w").write(
+    open(os.path.join(args.out_dir, f"{stem}_kernel_trace.md"), "w").write(
         "\n".join(lines) + "\n")
 
     # 2./3. byte counters, each counter in its own run
@@ -125,7 +145,7 @@ def main():
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         d, c = _rocprof(["--pmc", counter], bench_args + ["--steps", "2", "--warmup", "1"],
                         f"pass_{counter}", work, timeout=180)
-        res[("pass", counter)] = _counters(d, counter, "bcd_pass_kernel")
+        res[("pass", counter)] = _counters(d, counter, kernel)
         cmds[("pass", counter)] = c
         d, c = _rocprof(["--pmc", counter], [BENCH, "--copy-calibration"], f"copy_{counter}", work,
                         timeout=180)
@@ -133,13 +153,13 @@ def main():
         res[("copy", counter)] = vals
         cmds[("copy", counter)] = c
 
-    # 4. VALU instruction count of the pass kernel (wave-level instructions;
+    # 4. VALU instruction count of the kernel (wave-level instructions;
     #    x64 lanes = lane operations), for its VALU roofline
     d, c = _rocprof(["--pmc", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAVES"],
                     bench_args + ["--steps", "2", "--warmup", "1"], "pass_valu", work, timeout=180)
-    valu = _counters(d, "SQ_INSTS_VALU", "bcd_pass_kernel")
-    salu = _counters(d, "SQ_INSTS_SALU", "bcd_pass_kernel")
-    waves = _counters(d, "SQ_WAVES", "bcd_pass_kernel")
+    valu = _counters(d, "SQ_INSTS_VALU", kernel)
+    salu = _counters(d, "SQ_INSTS_SALU", kernel)
+    waves = _counters(d, "SQ_WAVES", kernel)
     cmds[("pass", "VALU")] = c
 
     copy_bytes = 256 << 20
@@ -153,15 +173,10 @@ def main():
     fetch_kib = sum(pf) / len(pf)
     write_kib = sum(pw) / len(pw)
     traffic = fetch_kib * 1024.0 * fetch_factor + write_kib * 1024.0 * write_factor
-    M, N = wl.spec.rows, wl.spec.cols
-    from calibration_free_bit_amd import dq
-    fmt = dq.FORMATS[wl.fmt]
-    b_alg = bench.alg_bytes_per_elem(2 if wl.spec.dtype == "bf16" else 4,
-                                     2 if fmt.a_fmt == dq.SCALE_FP16 else 1, fmt.group, M)
     rec = {
-        "workload": wl.name,
+        "workload": name,
         "source_hash": bench.kernel_source_hash(),
-        "kernel": "bcd_pass_kernel",
+        "kernel": kernel,
         "dispatches": len(pf),
         "fetch_kib_per_launch": fetch_kib,
         "write_kib_per_launch": write_kib,
@@ -178,21 +193,21 @@ def main():
         "valu_lane_ops_per_element": 64.0 * sum(valu) / len(valu) / (M * N),
         "commands": {f"{k[0]}_{k[1]}": v for k, v in cmds.items()},
     }
-    json.dump(rec, open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.json"), "w"), indent=2)
-    md = [f"# HBM byte counters: bcd_pass_kernel, workload {wl.name}", "",
-          f"Per pass launch (average of {len(pf)} dispatches): FETCH_SIZE {fetch_kib:.0f} KiB, "
+    json.dump(rec, open(os.path.join(args.out_dir, f"{stem}_counters.json"), "w"), indent=2)
+    md = [f"# HBM byte counters: {kernel}, workload {name}", "",
+          f"Per {launch} (average of {len(pf)} dispatches): FETCH_SIZE {fetch_kib:.0f} KiB, "
           f"WRITE_SIZE {write_kib:.0f} KiB.", "",
           f"Calibration: a plain 256 MiB device copy reads FETCH_SIZE {f_copy / 1024:.0f} KiB and "
           f"WRITE_SIZE {w_copy / 1024:.0f} KiB, so the factors are {fetch_factor:.4f} (fetch) and "
           f"{write_factor:.4f} (write).", "",
-          f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per weight "
-          f"element (algorithmic: {b_alg:.4f}).", "",
+          f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per {unit} "
+          f"(algorithmic: {b_alg:.4f}).", "",
           f"VALU: {rec['valu_insts_per_launch']:.4g} wave instructions per launch "
-          f"({rec['valu_lane_ops_per_element']:.2f} lane operations per weight element), "
+          f"({rec['valu_lane_ops_per_element']:.2f} lane operations per {unit}), "
           f"SALU {rec['salu_insts_per_launch']:.4g}, waves {rec['waves_per_launch']:.0f}.", "",
           "Commands:", ""]
     md += [f"    {v}" for v in cmds.values()]
-    open(os.path.join(args.out_dir, f"bcd_pass_{wl.name}_counters.md"), "w").write("\n".join(md) + "\n")
+    open(os.path.join(args.out_dir, f"{stem}_counters.md"), "w").write("\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
 
 

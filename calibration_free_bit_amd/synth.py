@@ -136,6 +136,42 @@ WORKLOADS = {
         "nvfp4_g16_4096x14336_bf16",
         MatrixSpec(4096, 14336, "normal", 0.01, 0.01, (25.0, 25.0), "bf16"),
         "nvfp4_g16", 20, (0, 1, 2)),
+    # the further MX formats, on the same 4096x4096 q_proj-shaped matrix
+    "mxfp4_g32_4096x4096_bf16": Workload(
+        "mxfp4_g32_4096x4096_bf16",
+        MatrixSpec(4096, 4096, "normal", 0.02, 0.01, (10.0, 50.0), "bf16"),
+        "mxfp4_g32", 20, (0, 1, 2)),
+    "mxint8_g32_4096x4096_bf16": Workload(
+        "mxint8_g32_4096x4096_bf16",
+        MatrixSpec(4096, 4096, "normal", 0.02, 0.01, (10.0, 50.0), "bf16"),
+        "mxint8_g32", 20, (0, 1, 2)),
+    "mxfp8_g32_4096x4096_bf16": Workload(
+        "mxfp8_g32_4096x4096_bf16",
+        MatrixSpec(4096, 4096, "normal", 0.02, 0.01, (10.0, 50.0), "bf16"),
+        "mxfp8_g32", 20, (0, 1, 2)),
+}
+
+
+@dataclass(frozen=True)
+class ActWorkload:
+    """Activation-side workload: X [tokens, cols] bf16 from make_activations,
+    column scales from make_col_scales, quantized in ``fmt``."""
+    name: str
+    tokens: int
+    cols: int
+    fmt: str
+    seed: int
+
+
+#: Activation quantization with the column scales folded in: a prefill batch
+#: of 8192 tokens entering the 4096-wide projections (q/k/v, gate/up) and
+#: the 14336-wide down projection of Llama-3.1-8B.
+ACT_WORKLOADS = {
+    w.name: w for w in (
+        ActWorkload("act_int4_g64_8192x4096_bf16", 8192, 4096, "int4_g64", 0),
+        ActWorkload("act_mxint4_g32_8192x4096_bf16", 8192, 4096, "mxint4_g32", 0),
+        ActWorkload("act_nvfp4_g16_8192x14336_bf16", 8192, 14336, "nvfp4_g16", 0),
+    )
 }
 
 #: The 224 linear layers of Llama-3.1-8B: 32 layers x 7 projections,
@@ -154,6 +190,15 @@ def llama_layer_specs():
             spec = MatrixSpec(M, N, "normal", 0.02, 0.01, (20.0, 20.0), "bf16")
             out.append((l, p, name, spec, 1000 * l + p))
     return out
+
+
+def make_col_scales(cols: int, seed: int) -> np.ndarray:
+    """fp16 bits of [cols] column inverse scales, log-uniform in [1/2, 2]
+    (the spread of solved column scales around 1), rounded to nearest even.
+    A stand-in for a solved b where only the activation side is measured."""
+    rng = np.random.default_rng(seed)
+    b = np.exp2(rng.uniform(-1.0, 1.0, size=cols))
+    return b.astype(np.float16).view(np.uint16)
 
 
 def make_activations(tokens: int, cols: int, seed: int, outlier_frac=0.01,

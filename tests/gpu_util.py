@@ -62,6 +62,12 @@ class DeviceRun:
         torch.cuda.synchronize()
         return self
 
+    def solve(self, iters: int):
+        """The same work as one dq_solve call (the benchmark's step)."""
+        self.s.solve(iters)
+        torch.cuda.synchronize()
+        return self
+
     @property
     def a(self):
         return decode_a(self.s.a, self.fmt)

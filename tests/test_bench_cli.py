@@ -46,3 +46,26 @@ def test_default_step_counts():
         ns = argparse.Namespace(steps=steps, warmup=warmup)
         bench._step_counts(ns, steps=100, warmup=200)
         assert (ns.steps, ns.warmup) == want
+
+
+def test_profile_stems_name_kernel_and_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    from calibration_free_bit_amd import synth
+
+    stems = {}
+    for name in list(synth.WORKLOADS) + list(synth.ACT_WORKLOADS):
+        stem = bench.profile_stem(name)
+        kernel = "act_quant_" if name in synth.ACT_WORKLOADS else "bcd_pass_"
+        assert stem.startswith(kernel)
+        assert stem.endswith(name.split("_", 1)[1] if name.startswith("act_") else name)
+        stems[stem] = name
+    assert len(stems) == len(synth.WORKLOADS) + len(synth.ACT_WORKLOADS)
+
+
+@pytest.mark.parametrize("name", ["act_no_such_workload", "int4_g64_1x1_bf16"])
+def test_unknown_workload_is_refused(name):
+    r = _run("--workload", name, "--no-cpu-baseline")
+    assert r.returncode == 2
+    assert "unknown workload" in r.stderr
+    assert r.stdout == ""

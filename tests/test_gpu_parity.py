@@ -446,19 +446,26 @@ def test_activation_rescale_quantize(name, tokens):
 
 # ------------------------------------------------------------ full-size workloads
 
-FULL = ["int4_g64_4096x4096_bf16", "mxint4_g32_14336x4096_bf16", "nvfp4_g16_4096x14336_bf16"]
+FULL = ["int4_g64_4096x4096_bf16", "mxint4_g32_14336x4096_bf16", "nvfp4_g16_4096x14336_bf16",
+        "mxfp4_g32_4096x4096_bf16", "mxint8_g32_4096x4096_bf16", "mxfp8_g32_4096x4096_bf16"]
 
 
 @pytest.mark.parametrize("wl_name", FULL)
 def test_full_size_sampled_stripes(wl_name):
     """The benchmarked configurations at full size, in the launch
-    configuration the benchmark times, checked on whole column stripes."""
+    configuration the benchmark times (one dq_solve per step), checked on
+    whole column stripes; the separate init / iterate / pack calls must
+    give the same bits."""
     wl = synth.WORKLOADS[wl_name]
     fmt = dq.FORMATS[wl.fmt]
     ofmt = oracle_fmt(fmt)
     m = synth.make_matrix(wl.spec, wl.seeds[0])
     print(f"[case] {wl_name} full solve T={wl.iters}", flush=True)
-    g = DeviceRun(m.data, fmt).run(wl.iters)
+    g = DeviceRun(m.data, fmt).solve(wl.iters)
+    sep = DeviceRun(m.data, fmt).run(wl.iters)
+    assert torch.equal(g.s.a, sep.s.a) and torch.equal(g.s.b, sep.s.b)
+    assert torch.equal(g.s.packed, sep.s.packed)
+    del sep
     a, b, Q = g.a, g.b, g.Q
     G = fmt.group
     n_str = m.spec.cols // G
@@ -477,6 +484,33 @@ def test_full_size_sampled_stripes(wl_name):
     from oracle import formats as F
     np.testing.assert_array_equal(F.project(a.ravel(), ofmt.a_fmt), a.ravel())
     np.testing.assert_array_equal(F.project(b, "fp16"), b)
+
+
+@pytest.mark.parametrize("aw_name", sorted(synth.ACT_WORKLOADS))
+def test_activation_full_size_sampled_tokens(aw_name):
+    """The benchmarked activation batches at full size, in the launch the
+    benchmark times; the oracle checks sampled whole tokens (each token is
+    quantized on its own)."""
+    aw = synth.ACT_WORKLOADS[aw_name]
+    fmt = dq.FORMATS[aw.fmt]
+    ofmt = oracle_fmt(fmt)
+    print(f"[case] {aw_name}", flush=True)
+    X = synth.make_activations(aw.tokens, aw.cols, aw.seed)
+    bbits = synth.make_col_scales(aw.cols, aw.seed + 1)
+    Xd = torch.from_numpy(X.view(np.int16)).cuda()
+    bd = torch.from_numpy(bbits.view(np.int16)).cuda()
+    xq = torch.empty((aw.tokens, aw.cols * fmt.code_bits // 8), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((aw.tokens, aw.cols // fmt.group), dtype=fmt.a_dtype, device="cuda")
+    p = dq.problem(1, aw.cols, fmt, dq.W_BF16, aw.cols)
+    dq.rescale_quantize_act(p, Xd, aw.tokens, aw.cols, bd, xq, xs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([[0, 1, aw.tokens - 1], rng.choice(aw.tokens, 29, replace=False)]))
+    b64 = bbits.view(np.float16).astype(np.float64)
+    codes, scales = D.rescale_quantize_act(synth.bf16_to_f64(X[toks]), b64, ofmt)
+    from tests.gpu_util import decode_a
+    np.testing.assert_array_equal(decode_a(xs[toks], fmt), scales)
+    np.testing.assert_array_equal(xq[toks].cpu().numpy(), D.pack_codes(codes, ofmt))
 
 
 def test_llama_layer_set_on_streams():
