@@ -72,6 +72,11 @@ __device__ __forceinline__ float quad_xor(float v) {
 __device__ __forceinline__ float half_mirror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
 }
+__device__ __forceinline__ double half_mirror(double v) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), 0x141, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), 0x141, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
 
 // ------------------------------------------------------------------ init
 
@@ -101,74 +106,145 @@ __global__ void __launch_bounds__(256) init_rtn_kernel(const void* __restrict__ 
 
 // ------------------------------------------- column-norm initialization
 
-// Partial column sums of |W| over chunks of chunk_rows rows: a workgroup
-// of 64 columns x 4 row-lanes per (tile, chunk); each lane adds every 4th
-// row of the chunk in order, then the 4 row-lanes are added pairwise.
+// Partial column sums of |W| over chunks of chunk_rows rows, one workgroup
+// per (tile, chunk). A lane owns 8 contiguous columns of every 32nd row of
+// the chunk (kColnormUnroll rows loaded before any is added) and adds its
+// rows in order; then the 32 row-lanes of each column are added in a fixed
+// tree (four runs of 8 through LDS, then the four runs by DPP).
+constexpr int kColnormUnroll = 8;
 template <int WT>
 __global__ void __launch_bounds__(256) colnorm_partial_kernel(const void* __restrict__ W, int64_t ldw,
                                                               int64_t M, int64_t N,
                                                               int64_t chunk_rows,
                                                               double* __restrict__ part) {
-  __shared__ double s_sum[4][kTileCols];
-  const int c = threadIdx.x & 63, rl = threadIdx.x >> 6;
+  constexpr int kRowLanes = 256 / (kTileCols / 8);  // 32
+  __shared__ double s_sum[kRowLanes][kTileCols];
+  const int c8 = threadIdx.x % (kTileCols / 8), rl = threadIdx.x / (kTileCols / 8);
   const int64_t tile = blockIdx.x, chunk = blockIdx.y;
-  const int64_t j = tile * kTileCols + c;
+  const int64_t col = tile * kTileCols + c8 * 8;
   const int64_t r0 = chunk * chunk_rows, r1 = min(r0 + chunk_rows, M);
-  double acc = 0.0;
-  if (j < N) {
-    for (int64_t r = r0 + rl; r < r1; r += 4) {
-      float v;
-      if constexpr (WT == kWBF16)
-        v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[r * ldw + j] << 16);
-      else
-        v = reinterpret_cast<const float*>(W)[r * ldw + j];
-      acc += (double)__builtin_fabsf(v);
+  double acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0;
+  if (col < N) {  // N is a multiple of 16: a lane's 8 columns are all in range or all out
+    for (int64_t r = r0 + rl; r < r1; r += kRowLanes * kColnormUnroll) {
+      float v[kColnormUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kColnormUnroll; ++u) {
+        const int64_t ru = min(r + (int64_t)kRowLanes * u, r1 - 1);  // rows past the chunk add 0
+        load8<WT>(W, ru * ldw + col, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kColnormUnroll; ++u) {
+        const bool in = r + (int64_t)kRowLanes * u < r1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += in ? (double)__builtin_fabsf(v[u][k]) : 0.0;
+      }
     }
   }
-  s_sum[rl][c] = acc;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s_sum[rl][c8 * 8 + k] = acc[k];
   __syncthreads();
-  if (rl == 0) part[(tile * gridDim.y + chunk) * kTileCols + c] = (s_sum[0][c] + s_sum[1][c]) +
-                                                                  (s_sum[2][c] + s_sum[3][c]);
+  const int c = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRowLanes / 4; ++i) t += s_sum[quarter * (kRowLanes / 4) + i][c];
+  t += quad_xor<1>(t);
+  t += quad_xor<2>(t);
+  if (quarter == 0) part[(tile * gridDim.y + chunk) * kTileCols + c] = t;
 }
 
 // b_j = Pi_fp16(sum_i |W_ij| / M), 1 for an all-zero column; the chunks are
-// added in order.
+// added in order, eight loads in flight at a time.
 static __global__ void __launch_bounds__(kTileCols) colnorm_b_kernel(const double* __restrict__ part,
                                                               int64_t n_chunks, int64_t M, int64_t N,
                                                               uint16_t* __restrict__ b) {
   const int64_t tile = blockIdx.x, j = tile * kTileCols + threadIdx.x;
   if (j >= N) return;
+  const double* __restrict__ pc = part + tile * n_chunks * kTileCols + threadIdx.x;
   double sum = 0.0;
-  for (int64_t k = 0; k < n_chunks; ++k) sum += part[(tile * n_chunks + k) * kTileCols + threadIdx.x];
+  for (int64_t k0 = 0; k0 < n_chunks; k0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = k0 + u < n_chunks ? pc[(k0 + u) * kTileCols] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
   const double bj = sum > 0.0 ? project<kScaleFp16>(sum / (double)M) : 1.0;
   b[j] = encode_scale<kScaleFp16>(bj);
 }
 
-// a = Pi_Fa(max_{j in block} |W_ij / b_j| / qmax), 1 for a zero block; the
-// quotients are correctly rounded float64 divisions.
+// a = Pi_Fa(max_{j in block} |W_ij / b_j| / qmax), 1 for a zero block. One
+// lane per 8 columns of kColnormRowsPerLane consecutive rows, G/8 lanes per
+// block (joined by DPP). The quotients are first formed in float32 from
+// 1-ulp reciprocals of b (relative error below 2^-22 after the division by
+// qmax) and projected on the certified path, which brackets that error; a
+// wave with any block it cannot certify recomputes its blocks from
+// correctly rounded float64 quotients, as the definition reads.
+constexpr int kColnormRowsPerLane = 4;
 template <int WT, int GRID, int AFMT, int G>
 __global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__ W, int64_t ldw,
                                                         int64_t M, int64_t N,
                                                         const uint16_t* __restrict__ b,
                                                         void* __restrict__ a_) {
   using AT = typename ScaleStore<AFMT>::T;
-  const int64_t nblk = N / G;
+  constexpr int R = kColnormRowsPerLane;
+  constexpr int LPB = G / 8;  // lanes per block; a block never straddles a wave
+  static_assert(LPB <= 8, "a block's lanes lie in one group of 8");
+  const int64_t nch = N / 8;
+  const int64_t n_rg = (M + R - 1) / R;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= M * nblk) return;
-  const int64_t row = idx / nblk, blk = idx - row * nblk;
-  double amax = 0.0;
+  const bool live = idx < n_rg * nch;
+  const int64_t cidx = live ? idx : 0;  // dead lanes compute on chunk 0
+  const int64_t rg = cidx / nch, col = (cidx - rg * nch) * 8;
+  float w[R][8];
 #pragma unroll
-  for (int c = 0; c < G / 8; ++c) {
-    float v[8];
-    load8<WT>(W, row * ldw + blk * G + 8 * c, v);
+  for (int u = 0; u < R; ++u) load8<WT>(W, min(rg * R + u, M - 1) * ldw + col, w[u]);
+  float bf[8], rb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    bf[k] = fp16_bits_to_float(b[col + k]);
+    rb[k] = __builtin_amdgcn_rcpf(bf[k]);
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int64_t r = rg * R + u;
+    float wmax = 0.0f, ymax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const double bj = (double)fp16_bits_to_float(b[blk * G + 8 * c + k]);
-      amax = __builtin_fmax(amax, (double)__builtin_fabsf(v[k]) / bj);
+      const float aw = __builtin_fabsf(w[u][k]);
+      wmax = __builtin_fmaxf(wmax, aw);
+      ymax = __builtin_fmaxf(ymax, aw * rb[k]);
     }
+    if constexpr (LPB >= 2) {
+      wmax = __builtin_fmaxf(wmax, quad_xor<1>(wmax));
+      ymax = __builtin_fmaxf(ymax, quad_xor<1>(ymax));
+    }
+    if constexpr (LPB >= 4) {
+      wmax = __builtin_fmaxf(wmax, quad_xor<2>(wmax));
+      ymax = __builtin_fmaxf(ymax, quad_xor<2>(ymax));
+    }
+    if constexpr (LPB >= 8) {
+      wmax = __builtin_fmaxf(wmax, half_mirror(wmax));
+      ymax = __builtin_fmaxf(ymax, half_mirror(ymax));
+    }
+    // a zero block is exactly the case wmax == 0; a non-zero block whose
+    // float32 quotients underflow is left to the certified path's range test
+    bool unsure = false;
+    float s = 1.0f;
+    if (wmax > 0.0f) s = ls_scale_fast<AFMT>((double)ymax, (double)Grid<GRID>::qmax, unsure);
+    if (wave_any(unsure)) {
+      double m = 0.0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = __builtin_fmax(m, (double)__builtin_fabsf(w[u][k]) / (double)bf[k]);
+      if constexpr (LPB >= 2) m = __builtin_fmax(m, quad_xor<1>(m));
+      if constexpr (LPB >= 4) m = __builtin_fmax(m, quad_xor<2>(m));
+      if constexpr (LPB >= 8) m = __builtin_fmax(m, half_mirror(m));
+      s = m > 0.0 ? (float)project<AFMT>(m / (double)Grid<GRID>::qmax) : 1.0f;
+    }
+    if (live && r < M && (threadIdx.x % LPB) == 0)
+      reinterpret_cast<AT*>(a_)[r * (N / G) + col / G] = encode_scale<AFMT>((double)s);
   }
-  const double s = amax > 0.0 ? project<AFMT>(amax / (double)Grid<GRID>::qmax) : 1.0;
-  reinterpret_cast<AT*>(a_)[idx] = encode_scale<AFMT>(s);
 }
 
 // ------------------------------------------------------------ BCD pass
@@ -879,7 +955,8 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
   colnorm_b_kernel<<<(unsigned)n_tiles, kTileCols, 0, st>>>(part, n_chunks, M, N, b);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  colnorm_a_kernel<WT, GRID, AFMT, G><<<blocks_for(M * (N / G), 256), 256, 0, st>>>(W, ldw, M, N, b, a);
+  const int64_t n_rg = (M + kColnormRowsPerLane - 1) / kColnormRowsPerLane;
+  colnorm_a_kernel<WT, GRID, AFMT, G><<<blocks_for(n_rg * (N / 8), 256), 256, 0, st>>>(W, ldw, M, N, b, a);
   return hipGetLastError();
 }
 
