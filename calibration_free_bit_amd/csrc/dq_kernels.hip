@@ -910,15 +910,28 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     float sf = ls_scale_fast<AFMT>((double)amax, (double)Grid<GRID>::qmax, unsure);
     if (wave_any(unsure))
       sf = amax > 0.0f ? (float)project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0f;
-    const float rs = __builtin_amdgcn_rcpf(sf);
     float y[8], q[8];
+    if constexpr (AFMT == kScaleE8M0 && (GRID == kGridInt4 || GRID == kGridInt8)) {
+      // a power-of-two scale: y = X b / s is exact (X b is, and so is the
+      // scaling by 2^-k down to the float32 subnormals, below any rounding
+      // decision), so rounding y itself is the exact decision
+      const float rs = __builtin_ldexpf(1.0f, 1 - __builtin_amdgcn_frexp_expf(sf));
+      constexpr float kClip = Grid<GRID>::qmax + 0.25f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
-    uint32_t diff[2];
-    if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
+      for (int k = 0; k < 8; ++k) {
+        y[k] = x[k] * rs;
+        q[k] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[k], -(kClip + (GRID == kGridInt4)), kClip));
+      }
+    } else {
+      const float rs = __builtin_amdgcn_rcpf(sf);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
+      for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
+      uint32_t diff[2];
+      if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
+      }
     }
     if (live && t < T) {
       Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
