@@ -18,6 +18,11 @@ With --workload llama31_8b_int4_g64_bf16 the step is instead the whole
 Llama-3.1-8B linear-layer set (32 layers x q, k, v, o, gate, up, down;
 6.98 G bf16 weights resident in HBM, INT4 G64, T = 20), every matrix solved
 (init, iterate, pack) with the matrices spread over --streams streams.
+The other single-matrix workloads (other shapes and formats) keep the same
+step; --init colnorm starts each solve from the column-norm start instead
+of absmax. With an act_... workload a step is one dq_rescale_quantize_act
+of a whole token batch (metric: activation elements/s; roofline of the
+activation kernel).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 (defaults: K = 100 timed steps after W = 200 warm-up steps for one matrix,
