@@ -162,6 +162,48 @@ def test_activation_e2m1_midpoints_and_neighbours():
     np.testing.assert_array_equal(xq.cpu().numpy(), D.pack_codes(codes, ofmt))
 
 
+@pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32"])
+def test_activation_integer_ties_power_of_two_scales(name):
+    # Under an E8M0 block scale the quotient X b / s is exact, so every
+    # half-integer below is an exact rounding tie (to even), decided without
+    # a tie flag; blocks at scales 2^-3 .. 2^3 (absmax qmax * 2^e), both
+    # signs, the bf16 neighbours of each tie, and values past the clip.
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    qmax = D.FORMATS[name].qmax
+    G, N = 32, 64
+    ties = np.arange(-qmax - 0.5, qmax + 1.0, 1.0)          # -qmax-0.5 .. qmax+0.5
+    vals = np.concatenate([ties, [qmax + 3.0, -qmax - 3.0, 0.0, 0.25]])
+    rows = []
+    for e in range(-3, 4):
+        blockvals = vals * 2.0 ** e
+        bits = synth.bf16_bits(blockvals)
+        nz = bits[blockvals != 0]
+        bits = np.concatenate([bits, nz + 1, nz - 1])         # the bf16 neighbours too
+        for start in range(0, len(bits), G - 1):
+            chunk = bits[start:start + G - 1]
+            row = np.zeros(G, dtype=np.uint16)
+            row[:len(chunk)] = chunk
+            row[G - 1] = synth.bf16_bits(np.array([qmax * 2.0 ** e]))[0]   # scale 2^e
+            rows.append(row)
+    if len(rows) % 2:
+        rows.append(rows[-1])
+    X = np.stack(rows).reshape(-1, N)                          # two blocks per token
+    tokens = X.shape[0]
+    b = torch.full((N,), 0x3C00, dtype=torch.int16, device="cuda")
+    p = dq.problem(tokens, N, fmt, dq.W_BF16, N)
+    xq = torch.empty((tokens, N * fmt.code_bits // 8), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((tokens, N // fmt.group), dtype=fmt.a_dtype, device="cuda")
+    print(f"[case] activation integer ties {name}, {tokens} tokens", flush=True)
+    dq.rescale_quantize_act(p, torch.from_numpy(X.view(np.int16)).cuda(), tokens, N, b, xq, xs)
+    torch.cuda.synchronize()
+    codes, scales = D.rescale_quantize_act(synth.bf16_to_f64(X), np.ones(N), ofmt)
+    from tests.gpu_util import decode_a
+    np.testing.assert_array_equal(decode_a(xs, fmt), scales)
+    np.testing.assert_array_equal(xq.cpu().numpy(), D.pack_codes(codes, ofmt))
+    assert np.any(D.code_ties(synth.bf16_to_f64(X), scales, np.ones(N), ofmt))
+
+
 def test_zero_slices():
     data = _mat(128, 256, 4)
     data[5, 64:128] = 0                # an all-zero block (bf16 zero bits)
@@ -276,6 +318,27 @@ def test_colnorm_init_then_iterate(name):
     sol = D.solve(W64, ofmt, 6, a=a0, b=b0)
     r = compare(W64, g.a, g.b, g.Q, sol, ofmt, f"colnorm {name}")
     assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
+
+
+@pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxint8_g32"])
+def test_colnorm_init_many_chunks_and_extreme_rows(name):
+    # 2600 rows: eleven 256-row chunks (the last one ragged), added in two
+    # batches per column; one row a factor 2^-100 down (its float32
+    # quotients leave the certified range, so those waves take the float64
+    # path), one 2^20 up, an all-zero column and an all-zero block
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    W = as_f64(_mat(2600, 320, 41))
+    W[5] *= 2.0 ** -100
+    W[1300] *= 2.0 ** 20
+    W[:, 33] = 0.0
+    W[2000, 128:192] = 0.0
+    data = synth.bf16_bits(W)
+    print(f"[case] colnorm init, many chunks, extreme rows {name}", flush=True)
+    g = _colnorm_run(data, fmt, 0)
+    a0, b0 = D.init_colnorm(as_f64(data), ofmt)
+    np.testing.assert_array_equal(g.b, b0)
+    np.testing.assert_array_equal(g.a, a0)
 
 
 # ------------------------------------------------------------ report
