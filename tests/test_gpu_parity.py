@@ -320,6 +320,21 @@ def test_colnorm_init_then_iterate(name):
     assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
 
 
+@pytest.mark.parametrize("dtype,ldw", [("bf16", 256), ("f32", 200)])
+def test_colnorm_init_padded_leading_dimension(dtype, ldw):
+    # the padding holds huge values: any read past the columns shows
+    fmt = NAMED["nvfp4_g16"]
+    ofmt = oracle_fmt(fmt)
+    data = _mat(300, 176, 43, dtype=dtype)
+    print(f"[case] colnorm init {dtype} ldw={ldw}", flush=True)
+    g = _colnorm_run(data, fmt, 2, ldw=ldw)
+    W64 = as_f64(data)
+    a0, b0 = D.init_colnorm(W64, ofmt)
+    sol = D.solve(W64, ofmt, 2, a=a0, b=b0)
+    r = compare(W64, g.a, g.b, g.Q, sol, ofmt, f"colnorm padded {dtype}")
+    assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
+
+
 @pytest.mark.parametrize("name", ["int4_g64", "mxint4_g32", "nvfp4_g16", "mxint8_g32"])
 def test_colnorm_init_many_chunks_and_extreme_rows(name):
     # 2600 rows: eleven 256-row chunks (the last one ragged), added in two
