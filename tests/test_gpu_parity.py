@@ -591,6 +591,31 @@ def test_activation_full_size_sampled_tokens(aw_name):
     np.testing.assert_array_equal(xq[toks].cpu().numpy(), D.pack_codes(codes, ofmt))
 
 
+def test_matrix_past_2_gib_uses_64_bit_offsets():
+    """A 32768 x 33024 bf16 matrix (2.16 GB): element offsets of the later
+    rows pass 2^31 bytes, so any 32-bit address arithmetic would read the
+    wrong rows. A seeded 4096-row block is tiled 8 times down the rows;
+    whole stripes at both ends and in the middle must match the oracle."""
+    fmt = NAMED["int4_g64"]
+    ofmt = oracle_fmt(fmt)
+    M, N, T = 32768, 33024, 2
+    block = _mat(4096, N, 61)
+    data = np.tile(block, (M // 4096, 1))
+    assert data.nbytes > 2 ** 31
+    print(f"[case] {M}x{N} bf16 ({data.nbytes / 2**30:.2f} GiB), T={T}", flush=True)
+    g = DeviceRun(data, fmt).solve(T)
+    a, b = g.a, g.b
+    packed = g.s.packed
+    G = fmt.group
+    for s in (0, N // G // 2, N // G - 1):
+        cs = slice(s * G, s * G + G)
+        Ws = synth.bf16_to_f64(data[:, cs])
+        sol = D.solve(Ws, ofmt, T)
+        Qs = D.unpack_codes(packed[:, s * G // 2:(s + 1) * G // 2].cpu().numpy(), ofmt)
+        r = compare(Ws, a[:, s:s + 1], b[cs], Qs, sol, ofmt, f"large stripe {s}")
+        assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, (s, r)
+
+
 def test_llama_layer_set_on_streams():
     """Layer 0 of the Llama-3.1-8B linear set (all seven shapes of the set:
     q, k, v, o, gate, up, down) solved together with the matrices spread over
