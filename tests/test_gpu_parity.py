@@ -616,6 +616,31 @@ def test_matrix_past_2_gib_uses_64_bit_offsets():
         assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, (s, r)
 
 
+def test_activation_batch_past_2_gib_uses_64_bit_offsets():
+    """77824 tokens x 14336 channels of bf16 (2.23 GB; a seeded 4096-token
+    block tiled down the tokens), NVFP4: tokens past 2^31 bytes must be
+    quantized from their own rows."""
+    fmt = NAMED["nvfp4_g16"]
+    ofmt = oracle_fmt(fmt)
+    T, N = 77824, 14336
+    X = np.tile(synth.make_activations(4096, N, 67), (T // 4096, 1))
+    assert X.nbytes > 2 ** 31
+    bbits = synth.make_col_scales(N, 68)
+    print(f"[case] activations {T}x{N} ({X.nbytes / 2**30:.2f} GiB)", flush=True)
+    Xd = torch.from_numpy(X.view(np.int16)).cuda()
+    bd = torch.from_numpy(bbits.view(np.int16)).cuda()
+    xq = torch.empty((T, N // 2), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((T, N // fmt.group), dtype=fmt.a_dtype, device="cuda")
+    dq.rescale_quantize_act(dq.problem(1, N, fmt, dq.W_BF16, N), Xd, T, N, bd, xq, xs)
+    torch.cuda.synchronize()
+    toks = np.array([0, 4095, 4096, T // 2 + 17, T - 4097, T - 2, T - 1])
+    codes, scales = D.rescale_quantize_act(synth.bf16_to_f64(X[toks]),
+                                           bbits.view(np.float16).astype(np.float64), ofmt)
+    from tests.gpu_util import decode_a
+    np.testing.assert_array_equal(decode_a(xs[toks], fmt), scales)
+    np.testing.assert_array_equal(xq[toks].cpu().numpy(), D.pack_codes(codes, ofmt))
+
+
 def test_llama_layer_set_on_streams():
     """Layer 0 of the Llama-3.1-8B linear set (all seven shapes of the set:
     q, k, v, o, gate, up, down) solved together with the matrices spread over
