@@ -40,6 +40,11 @@ enum : int { kWF32 = 0, kWBF16 = 1 };
 // quotients up to 8.25; the int8 grid (quotients up to 127.25) uses
 // 0.5 - 2^-13. The estimate's relative error is below 7 * 2^-24.
 constexpr float kTieFlag = 0.5f - 0x1p-17f;
+
+// 1 / a, exactly, for a power of two a (float32, subnormals included).
+__device__ __forceinline__ float recip_pow2(float a) {
+  return __builtin_ldexpf(1.0f, 1 - __builtin_amdgcn_frexp_expf(a));
+}
 constexpr float kTieFlag8 = 0.5f - 0x1p-13f;
 
 // ------------------------------------------------------------ scale codes
@@ -213,6 +218,12 @@ template <> struct Grid<kGridInt4> {
                                               int e) {
     return __builtin_fabsf(__builtin_amdgcn_fmed3f(y[e], -8.25f, 7.25f) - q[e]) > kTieFlag;
   }
+  // Codes of N quotients that are exact (rounding them is the decision).
+  template <int N>
+  __device__ static __forceinline__ void nearest_n(const float* y, float* q) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) q[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[e], -8.25f, 7.25f));
+  }
   // Nibbles of 8 codes, element k in bits 4k..4k+3.
   __device__ static __forceinline__ uint32_t pack8(const float* q) {
     uint32_t w = 0u;
@@ -296,6 +307,25 @@ template <> struct Grid<kGridE2M1> {
                                               int e) {
     return ((diff[e >> 3] >> (4 * (e & 7))) & 0xFu) != 0u;
   }
+  // Codes of N quotients that are exact: the conversion's own rounding is
+  // the decision (a zero may come back as -0).
+  template <int N>
+  __device__ static __forceinline__ void nearest_n(const float* y, float* q) {
+    static_assert(N % 8 == 0, "groups of 8");
+#pragma unroll
+    for (int g = 0; g < N; g += 8) {
+      float yc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) yc[k] = __builtin_amdgcn_fmed3f(y[g + k], -8.0f, 8.0f);
+      const uint32_t w = cvt8(yc);
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 r;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); q[g + 0] = r.x; q[g + 1] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); q[g + 2] = r.x; q[g + 3] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); q[g + 4] = r.x; q[g + 5] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); q[g + 6] = r.x; q[g + 7] = r.y;
+    }
+  }
   // Nibbles of 8 codes (exact E2M1 values, so the conversion is exact);
   // a zero is stored as +0.
   __device__ static __forceinline__ uint32_t pack8(const float* q) {
@@ -341,6 +371,12 @@ template <> struct Grid<kGridInt8> {
   __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
                                               int e) {
     return __builtin_fabsf(__builtin_amdgcn_fmed3f(y[e], -127.25f, 127.25f) - q[e]) > kTieFlag8;
+  }
+  // Codes of N quotients that are exact (rounding them is the decision).
+  template <int N>
+  __device__ static __forceinline__ void nearest_n(const float* y, float* q) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) q[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[e], -127.25f, 127.25f));
   }
   // 8 codes as two's complement bytes (8 bytes, 8-byte aligned when stored).
   using Word = uint2;
@@ -416,6 +452,23 @@ template <> struct Grid<kGridE4M3> {
   __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
                                               int e) {
     return ((diff[e >> 2] >> (8 * (e & 3))) & 0xFFu) != 0u;
+  }
+  // Codes of N quotients that are exact: the conversion's own rounding is
+  // the decision (magnitudes up to 456 saturate to 448).
+  template <int N>
+  __device__ static __forceinline__ void nearest_n(const float* y, float* q) {
+    static_assert(N % 4 == 0, "groups of 4");
+#pragma unroll
+    for (int g = 0; g < N; g += 4) {
+      float yc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) yc[k] = __builtin_amdgcn_fmed3f(y[g + k], -456.0f, 456.0f);
+      const uint32_t w = cvt4(yc);
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 r;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false); q[g + 0] = r.x; q[g + 1] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);  q[g + 2] = r.x; q[g + 3] = r.y;
+    }
   }
   // 8 codes as E4M3 bytes (exact values; a zero as +0), 8 bytes.
   using Word = uint2;

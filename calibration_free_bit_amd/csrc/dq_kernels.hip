@@ -358,6 +358,10 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
   using Word = typename Grid<GRID>::Word;
   constexpr bool STATS = MODE == kPassStats;
   constexpr bool INIT = MODE == kPassInit;
+  // The first pass of a whole solve under power-of-two block scales: with
+  // b = 1 and a = 2^k the quotient W / (a b) is exact, so rounding it is the
+  // decision itself (no tie flag, no exact re-decision).
+  constexpr bool kExactQ = INIT && AFMT == kScaleE8M0;
   constexpr int CB = Grid<GRID>::kBits;     // bits per stored code
   constexpr int LC = kLaneCols;             // contiguous columns per lane
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
@@ -550,24 +554,29 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       {
         float ra[NB], y[LC];
 #pragma unroll
-        for (int bl = 0; bl < NB; ++bl) ra[bl] = __builtin_amdgcn_rcpf(a_old[bl]);
+        for (int bl = 0; bl < NB; ++bl)
+          ra[bl] = kExactQ ? recip_pow2(a_old[bl]) : __builtin_amdgcn_rcpf(a_old[bl]);
 #pragma unroll
         for (int e = 0; e < LC; ++e) wrb[e] = w[e] * LRB(e);
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
-        uint32_t diff[LC / 4];
-        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
-          // only the element slots where some lane is near a midpoint
+        if constexpr (kExactQ) {
+          Grid<GRID>::template nearest_n<LC>(y, q);
+        } else {
+          uint32_t diff[LC / 4];
+          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
+            // only the element slots where some lane is near a midpoint
 #pragma unroll
-          for (int bl = 0; bl < NB; ++bl)
+            for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-            for (int k = 0; k < BL; ++k) {
-              const int e = bl * BL + k;
-              if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], LB(e));
-            }
+              for (int k = 0; k < BL; ++k) {
+                const int e = bl * BL + k;
+                if (wave_any(Grid<GRID>::near(y, q, diff, e)))
+                  q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], LB(e));
+              }
+          }
         }
         row_sums();
       }
@@ -627,20 +636,24 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         float y[LC];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-          const float ra = __builtin_amdgcn_rcpf(a_new[bl]);
+          const float ra = kExactQ ? recip_pow2(a_new[bl]) : __builtin_amdgcn_rcpf(a_new[bl]);
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra;
         }
-        uint32_t diff[LC / 4];
-        if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
+        if constexpr (kExactQ) {
+          Grid<GRID>::template nearest_n<LC>(y, q);
+        } else {
+          uint32_t diff[LC / 4];
+          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
 #pragma unroll
-          for (int bl = 0; bl < NB; ++bl)
+            for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-            for (int k = 0; k < BL; ++k) {
-              const int e = bl * BL + k;
-              if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], LB(e));
-            }
+              for (int k = 0; k < BL; ++k) {
+                const int e = bl * BL + k;
+                if (wave_any(Grid<GRID>::near(y, q, diff, e)))
+                  q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], LB(e));
+              }
+          }
         }
       }
 
