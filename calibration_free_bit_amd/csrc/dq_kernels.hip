@@ -924,17 +924,14 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     if (wave_any(unsure))
       sf = amax > 0.0f ? (float)project<AFMT>((double)amax / (double)Grid<GRID>::qmax) : 1.0f;
     float y[8], q[8];
-    if constexpr (AFMT == kScaleE8M0 && (GRID == kGridInt4 || GRID == kGridInt8)) {
+    if constexpr (AFMT == kScaleE8M0) {
       // a power-of-two scale: y = X b / s is exact (X b is, and so is the
       // scaling by 2^-k down to the float32 subnormals, below any rounding
       // decision), so rounding y itself is the exact decision
-      const float rs = __builtin_ldexpf(1.0f, 1 - __builtin_amdgcn_frexp_expf(sf));
-      constexpr float kClip = Grid<GRID>::qmax + 0.25f;
+      const float rs = recip_pow2(sf);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        y[k] = x[k] * rs;
-        q[k] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[k], -(kClip + (GRID == kGridInt4)), kClip));
-      }
+      for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
+      Grid<GRID>::template nearest_n<8>(y, q);
     } else {
       const float rs = __builtin_amdgcn_rcpf(sf);
 #pragma unroll

@@ -162,6 +162,43 @@ def test_activation_e2m1_midpoints_and_neighbours():
     np.testing.assert_array_equal(xq.cpu().numpy(), D.pack_codes(codes, ofmt))
 
 
+def test_activation_e4m3_midpoints_and_neighbours():
+    # Blocks whose absmax is 448 get the E8M0 scale 1 with b = 1, so the
+    # codes are the E4M3 rounding of the values themselves: the midpoints
+    # between neighbouring E4M3 values from 2^-9 up to 448 that bf16 holds
+    # exactly, their bf16 neighbours, values past 448, both signs.
+    fmt = NAMED["mxfp8_g32"]
+    ofmt = oracle_fmt(fmt)
+    from oracle import formats as F
+    lv = F.e4m3_levels()
+    lv = lv[lv > 0]
+    mids = (lv[:-1] + lv[1:]) / 2
+    mb = synth.bf16_bits(mids)
+    mb = mb[synth.bf16_to_f64(mb) == mids]                      # midpoints bf16 holds exactly
+    pos = np.concatenate([mb, mb - 1, mb + 1, synth.bf16_bits(np.array([450.0, 460.0, 500.0]))])
+    bits = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
+    N = 32
+    tokens = (len(bits) + N - 2) // (N - 1)
+    tokens += tokens % 2
+    X = np.zeros((tokens, N), dtype=np.uint16)
+    flat = np.zeros(tokens * (N - 1), dtype=np.uint16)
+    flat[:len(bits)] = bits
+    X[:, :N - 1] = flat.reshape(tokens, N - 1)
+    X[:, N - 1] = synth.bf16_bits(np.array([448.0]))[0]        # absmax 448 -> scale 1
+    X = X.reshape(-1, 2 * N)                                    # two blocks per token
+    tokens, N = X.shape
+    b = torch.full((N,), 0x3C00, dtype=torch.int16, device="cuda")
+    p = dq.problem(tokens, N, fmt, dq.W_BF16, N)
+    xq = torch.empty((tokens, N), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((tokens, N // fmt.group), dtype=fmt.a_dtype, device="cuda")
+    print(f"[case] activation E4M3 midpoints, {tokens} tokens", flush=True)
+    dq.rescale_quantize_act(p, torch.from_numpy(X.view(np.int16)).cuda(), tokens, N, b, xq, xs)
+    torch.cuda.synchronize()
+    codes, scales = D.rescale_quantize_act(synth.bf16_to_f64(X), np.ones(N), ofmt)
+    np.testing.assert_array_equal(xq.cpu().numpy(), D.pack_codes(codes, ofmt))
+    assert np.any(D.code_ties(synth.bf16_to_f64(X), scales, np.ones(N), ofmt))
+
+
 @pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32"])
 def test_activation_integer_ties_power_of_two_scales(name):
     # Under an E8M0 block scale the quotient X b / s is exact, so every
