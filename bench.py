@@ -1,32 +1,32 @@
 """Benchmark of the DualQuant BCD solver on one MI355X.
 
-A step is one pass of the whole hot path over one synthetic weight matrix:
-dq_init_rtn (absmax RTN), dq_bcd_iterate(T) and dq_pack_codes, with W
-already resident in HBM. The workload is a 4096x4096 bf16 q_proj-shaped
-matrix, N(0, 0.02^2) with 1 % outlier columns scaled by U[10, 50], INT4
-codes, G = 64, fp16 block and column scales, T = 20 iterations.
+Default workload: the whole Llama-3.1-8B linear-layer set (32 layers x q,
+k, v, o, gate, up, down; 224 matrices, 6.98 G bf16 weights, 13.96 GB,
+resident in HBM; N(0, 0.02^2) with 1 % outlier columns x 20; INT4 codes,
+G = 64, fp16 block and column scales, T = 20 iterations). A step solves
+every matrix of the set (absmax start, T iterations, packed codes; one
+dq_solve each), the matrices spread over --streams streams.
 
-value = rows * cols * T * steps / (time of the timed steps): weight elements
-per second per BCD iteration, whole job (init and pack included). The
-roofline entry is for the dominant kernel, the BCD pass: its algorithmic
-bytes per launch (one read of W plus a read and a write of the block scales
-and the column scales) over its average duration, measured with events on
-the stream the kernel runs on. cpu_baseline times the float64 oracle on
-the host (test infrastructure, never on the product path).
+value = set elements * T / step time: weight elements per second per BCD
+iteration, whole job (start and packing included). The roofline entry is
+for the dominant kernel, the BCD pass, on the dominant shape (gate/up,
+14336 x 4096, 54 % of the set's elements): its algorithmic bytes per
+launch (one read of W plus a read and a write of the block scales and the
+column scales) over its average duration, measured in this run with events
+on the stream it runs on, T passes at a time on one resident gate matrix
+after the timed steps. cpu_baseline times the float64 oracle (test
+infrastructure, never on the product path) on the whole of layer 0 with a
+pool of worker processes.
 
-With --workload llama31_8b_int4_g64_bf16 the step is instead the whole
-Llama-3.1-8B linear-layer set (32 layers x q, k, v, o, gate, up, down;
-6.98 G bf16 weights resident in HBM, INT4 G64, T = 20), every matrix solved
-(init, iterate, pack) with the matrices spread over --streams streams.
-The other single-matrix workloads (other shapes and formats) keep the same
-step; --init colnorm starts each solve from the column-norm start instead
-of absmax. With an act_... workload a step is one dq_rescale_quantize_act
-of a whole token batch (metric: activation elements/s; roofline of the
-activation kernel).
+--workload NAME selects a single-matrix workload instead (other shapes and
+formats; --init colnorm starts each solve from the column-norm start), with
+the same step (one whole solve) and the roofline of its own pass kernel, or
+an activation workload act_... (a step is one dq_rescale_quantize_act of a
+whole token batch; metric: activation elements/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-(defaults: K = 100 timed steps after W = 200 warm-up steps for one matrix,
-K = 10 after W = 2 for the layer set).
+(defaults: K = 10 timed steps after W = 2 warm-up steps for the layer set;
+K = 100 after W = 200 for a single matrix or an activation batch).
 """
 
 from __future__ import annotations
@@ -155,58 +155,86 @@ def _make_set_matrix(item):
     return l, p, synth.make_matrix(spec, seed).data
 
 
-def set_cpu_baseline(items, budget_s: float = 15.0):
-    """The float64 oracle on a bounded sample of the set: the leading column
-    stripes of each of layer 0's seven matrices, as many per matrix as fit
-    the budget (sized from a first run on two stripes each)."""
-    from oracle import dualquant as D
+#: Columns per task of the set's oracle baseline (whole stripes of G = 64).
+SET_BASELINE_CHUNK_COLS = 512
+
+
+def _oracle_chunk(task):
+    """Worker of the set's oracle baseline: the float64 oracle on one column
+    block (whole stripes) of one matrix, T iterations; returns its elements."""
     from calibration_free_bit_amd import synth
-    fmt = D.FORMATS["int4_g64"]
-    G = fmt.group
-    layer0 = [(name, synth.bf16_to_f64(synth.make_matrix(spec, seed).data))
-              for (l, p, name, spec, seed) in items[:7]]
+    from oracle import dualquant as D
+    bits, iters = task
+    W = synth.bf16_to_f64(bits)
+    D.solve(W, D.FORMATS["int4_g64"], iters)
+    return W.size
 
-    def run(k):
-        t0 = time.perf_counter()
-        n = 0
-        for name, W in layer0:
-            Ws = W[:, :k * G]
-            D.solve(Ws, fmt, 20)
-            n += Ws.size
-        return n, time.perf_counter() - t0
 
-    n, dt = run(2)
-    k = max(2, min(min(W.shape[1] for _, W in layer0) // G, int(2 * budget_s / max(dt, 1e-3))))
-    n, dt = run(k)
-    return {"value": n * 20 / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 numpy oracle, the first {k} column stripes (G={G}) of each of layer 0's "
-                      f"seven matrices ({', '.join(f'{nm} {W.shape[0]}x{k * G}' for nm, W in layer0)}); "
-                      f"T=20, {dt:.1f} s"}
+def set_cpu_baseline(pool, n_proc: int, layer0, iters: int):
+    """The float64 oracle on the whole of layer 0 (its seven matrices, 218 M
+    weights), split into blocks of whole column stripes -- which the method
+    solves independently of each other, so the blocks together are exactly
+    the layer's solve -- on a pool of n_proc worker processes (forked before
+    the GPU was touched). Reported as elements/s per iteration; the full set
+    is 32 such layers ("x32 extrapolated" for its time)."""
+    tasks = []
+    for name, bits in layer0:
+        for c0 in range(0, bits.shape[1], SET_BASELINE_CHUNK_COLS):
+            tasks.append((name, bits[:, c0:c0 + SET_BASELINE_CHUNK_COLS]))
+    # largest blocks first, so the pool drains evenly
+    tasks.sort(key=lambda t: -t[1].size)
+    t0 = time.perf_counter()
+    n = sum(pool.imap_unordered(_oracle_chunk, [(b, iters) for _, b in tasks], chunksize=1))
+    dt = time.perf_counter() - t0
+    rate = n * iters / dt
+    shapes = ", ".join(f"{nm} {b.shape[0]}x{b.shape[1]}" for nm, b in layer0)
+    return {"value": rate, "unit": "elements/s", "cores": n_proc, "kind": "oracle",
+            "sample": f"float64 numpy oracle on all of layer 0 ({shapes}; {n} weights) in "
+                      f"{len(tasks)} blocks of up to {SET_BASELINE_CHUNK_COLS} columns, T={iters}, "
+                      f"{n_proc} worker processes (host affinity {len(os.sched_getaffinity(0))} cores), "
+                      f"{dt:.1f} s; x32 extrapolated, the whole set would take "
+                      f"{32 * n * iters / rate:.0f} s"}
+
+
+def baseline_workers() -> int:
+    """Worker processes for host-side work: the cores this process may run
+    on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def run_set(args):
     """The whole Llama-3.1-8B linear set on one GPU, spread over streams."""
     import multiprocessing as mp
+
+    import numpy as np
+
     from calibration_free_bit_amd import synth
     items = synth.llama_layer_specs()
-    # host generation in worker processes forked before the GPU is touched
-    n_proc = max(1, min(16, len(os.sched_getaffinity(0))))
+    # host generation and the oracle baseline in worker processes forked
+    # before the GPU is touched
+    n_proc = baseline_workers()
     pool = mp.get_context("fork").Pool(n_proc)
-    import numpy as np
+    t_gen = time.perf_counter()
+    host = {}
+    for l, p, data in pool.imap_unordered(_make_set_matrix, items, chunksize=1):
+        host[(l, p)] = data
+    t_gen = time.perf_counter() - t_gen
+    T = 20
+    baseline = None
+    if not args.no_cpu_baseline:
+        layer0 = [(name, host[(l, p)]) for (l, p, name, _, _) in items if l == 0]
+        baseline = set_cpu_baseline(pool, n_proc, layer0, T)
+    pool.close()
+    pool.join()
+
     import torch
     from calibration_free_bit_amd import dq
     fmt = dq.FORMATS["int4_g64"]
-    T = 20
-    t_gen = time.perf_counter()
-    solvers = [None] * len(items)
-    index = {(l, p): k for k, (l, p, _, _, _) in enumerate(items)}
-    for l, p, data in pool.imap_unordered(_make_set_matrix, items, chunksize=1):
-        W = torch.from_numpy(data.view(np.int16)).to("cuda:0")
-        solvers[index[(l, p)]] = dq.Solver(W, fmt)
-    pool.close()
-    pool.join()
+    solvers = []
+    for (l, p, name, spec, seed) in items:
+        W = torch.from_numpy(host.pop((l, p)).view(np.int16)).to("cuda:0")
+        solvers.append(dq.Solver(W, fmt))
     torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
     elems = sum(s.W.numel() for s in solvers)
     streams = [torch.cuda.Stream() for _ in range(args.streams)]
     cur = torch.cuda.current_stream()
@@ -224,8 +252,27 @@ def run_set(args):
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / args.steps
     value = elems * T / (step_ms * 1e-3)
-    b_alg = alg_bytes_per_elem(2, 2, fmt.group, 4096)
-    achieved = value * b_alg / 1e9  # whole step, init and pack included
+    b_step = alg_bytes_per_elem(2, 2, fmt.group, 4096)
+    step_gbs = value * b_step / 1e9  # whole step, start and packing included
+
+    # the dominant kernel on the dominant shape: T passes at a time of layer
+    # 0's gate matrix (14336 x 4096), alone on the current stream, timed with
+    # events on that stream (each T includes one final column update)
+    gate = solvers[[k for k, it in enumerate(items) if it[2] == "gate"][0]]
+    M, N = gate.W.shape
+    reps = max(3, args.steps)
+    gate.iterate(T)  # warm
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(cur)
+    for _ in range(reps):
+        gate.iterate(T)
+    r1.record(cur)
+    torch.cuda.synchronize()
+    pass_s = r0.elapsed_time(r1) * 1e-3 / (reps * T)
+    b_pass = alg_bytes_per_elem(2, 2, fmt.group, M)
+    achieved = b_pass * M * N / pass_s / 1e9
+    dom = f"int4_g64_{M}x{N}_bf16"
     out = {
         "metric": "weight elements/s per BCD iteration",
         "value": value,
@@ -243,13 +290,18 @@ def run_set(args):
                    "format": "int4_g64", "iters": T, "streams": args.streams,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "whole step (every kernel of the set, overlapped on streams)",
-                     "alg_bytes_per_elem": b_alg},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(dom),
+                     "kernel": f"bcd_pass_kernel on the gate/up shape {M}x{N} INT4-G64 (layer 0 gate)",
+                     "alg_bytes_per_elem": b_pass, "avg_launch_us": pass_s * 1e6,
+                     "launches": reps * T, "counters": f"profiles/{profile_stem(dom)}_counters.json"},
+        "valu": valu_entry(recorded_valu(dom), pass_s, M * N),
+        "whole_step": {"achieved": step_gbs, "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                       "alg_bytes_per_elem": b_step,
+                       "note": "every kernel of the set, overlapped on the streams"},
         "breakdown_ms": {"wall_per_step": wall * 1e3 / args.steps, "host_generation_s": t_gen},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = set_cpu_baseline(items)
+    if baseline is not None:
+        out["cpu_baseline"] = baseline
     print(json.dumps(out))
 
 
@@ -270,7 +322,7 @@ def main():
     # the layer set 10 after 2
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
+    ap.add_argument("--workload", default=SET_WORKLOAD)
     ap.add_argument("--streams", type=int, default=2, help="streams of the Llama set workload")
     ap.add_argument("--init", choices=("rtn", "colnorm"), default="rtn",
                     help="start of a single-matrix solve: absmax (default) or the column-norm start")
@@ -396,6 +448,7 @@ def main():
         "breakdown_ms": {"init": init_ms, "iterate": iter_ms, "pack": pack_ms,
                          "wall_per_step": wall * 1e3 / args.steps},
         "iterate_elements_per_s_per_iter": elems / pass_s,
+        "us_per_iter": iter_ms * 1e3 / T,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data)

@@ -89,41 +89,6 @@ Workspace pass_geometry(const dq_problem* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DQ_OK : DQ_ERR_HIP; }
 
-// Calls f.template operator()<WT, GRID, AFMT, G>() for p's format.
-template <class F>
-int dispatch(const dq_problem& p, F&& f) {
-  auto by_group = [&]<int WT, int GR, int AF>() -> int {
-    switch (p.group) {
-      case 16: return f.template operator()<WT, GR, AF, 16>();
-      case 32: return f.template operator()<WT, GR, AF, 32>();
-      case 64: return f.template operator()<WT, GR, AF, 64>();
-    }
-    return DQ_ERR_UNSUPPORTED;
-  };
-  auto by_afmt = [&]<int WT, int GR>() -> int {
-    switch (p.a_fmt) {
-      case DQ_SCALE_FP16: return by_group.template operator()<WT, GR, dq::kScaleFp16>();
-      case DQ_SCALE_E8M0: return by_group.template operator()<WT, GR, dq::kScaleE8M0>();
-      case DQ_SCALE_E4M3: return by_group.template operator()<WT, GR, dq::kScaleE4M3>();
-    }
-    return DQ_ERR_UNSUPPORTED;
-  };
-  auto by_grid = [&]<int WT>() -> int {
-    switch (p.grid) {
-      case DQ_GRID_INT4: return by_afmt.template operator()<WT, dq::kGridInt4>();
-      case DQ_GRID_E2M1: return by_afmt.template operator()<WT, dq::kGridE2M1>();
-      case DQ_GRID_INT8: return by_afmt.template operator()<WT, dq::kGridInt8>();
-      case DQ_GRID_E4M3: return by_afmt.template operator()<WT, dq::kGridE4M3>();
-    }
-    return DQ_ERR_UNSUPPORTED;
-  };
-  switch (p.w_type) {
-    case DQ_W_F32: return by_grid.template operator()<dq::kWF32>();
-    case DQ_W_BF16: return by_grid.template operator()<dq::kWBF16>();
-  }
-  return DQ_ERR_UNSUPPORTED;
-}
-
 }  // namespace
 
 extern "C" {
@@ -180,7 +145,7 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
   if (int s = check_problem(p)) return s;
   if (!W || !a || !b || !aligned16(W) || n_iters < 0) return DQ_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(stats) & 7u) return DQ_ERR_INVALID_ARG;
-  if (n_iters == 0) return DQ_OK;
+  if (n_iters == 0 && !stats) return DQ_OK;
   const Workspace ws = pass_geometry(p);
   if (!workspace || workspace_bytes < (stats ? ws.stats_bytes : ws.bytes) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -191,6 +156,9 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
                           reinterpret_cast<double*>(base + ws.pass_bytes + ws.codes_bytes)};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    if (n_iters == 0)  // row 0 alone: the state passed in, no code changed
+      return hip_status(dq::launch_report<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, nullptr,
+                                                         nullptr, stats, its.part, st));
     return hip_status(
         dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, false, st));
   });

@@ -57,6 +57,19 @@ template <> struct ScaleStore<kScaleFp16> { using T = uint16_t; };
 template <> struct ScaleStore<kScaleE8M0> { using T = uint8_t; };
 template <> struct ScaleStore<kScaleE4M3> { using T = uint8_t; };
 
+// 1 / a for a block scale of format AFMT. E8M0 scales reach 2^-127, a
+// float32 subnormal, which the hardware reciprocal does not take, so they
+// use the exact power-of-two reciprocal; fp16 (>= 2^-24) and E4M3 (>= 2^-9)
+// scales are normal float32 values and take the 1-ulp hardware reciprocal.
+template <int AFMT>
+__device__ __forceinline__ float recip_scale(float a) {
+  if constexpr (AFMT == kScaleE8M0) {
+    return recip_pow2(a);
+  } else {
+    return __builtin_amdgcn_rcpf(a);
+  }
+}
+
 __device__ __forceinline__ float fp16_bits_to_float(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }

@@ -10,10 +10,7 @@ namespace dq {
 constexpr int kTileCols = 64;   // columns of one independent tile
 constexpr int kLaneCols = 16;   // contiguous columns one lane owns
 constexpr int kRowsPerStep = 4 * 64 * kLaneCols / kTileCols;  // rows per workgroup step
-#ifndef DQ_PASS_GRID
-#define DQ_PASS_GRID 512
-#endif
-constexpr int kPassGrid = DQ_PASS_GRID;  // target workgroups of one BCD pass
+constexpr int kPassGrid = 512;  // target workgroups of one BCD pass (two per CU)
 
 // Geometry of one BCD pass. Work is the flattened list of (tile, row step)
 // pairs, tile-major; workgroup w owns steps [w L, (w+1) L). The workgroups

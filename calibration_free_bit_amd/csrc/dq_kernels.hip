@@ -250,19 +250,8 @@ __global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__
 // ------------------------------------------------------------ BCD pass
 
 constexpr int kThreads = 256;  // 4 waves
-#ifndef DQ_PREFETCH
-#define DQ_PREFETCH 1
-#endif
-constexpr int kPrefetch = DQ_PREFETCH;  // row steps in flight per lane
-#ifndef DQ_ROW_CHAINS
-#define DQ_ROW_CHAINS 1  // independent partial sums per block in the row update
-#endif
-#ifndef DQ_B_IN_REGS
-#define DQ_B_IN_REGS 0
-#endif
-#ifndef DQ_PASS_OCC
-#define DQ_PASS_OCC 2  // workgroups per CU the register budget must allow
-#endif
+constexpr int kPrefetch = 1;   // row steps in flight per lane
+constexpr int kPassOcc = 2;    // workgroups per CU the register budget must allow
 
 // Column update from the partials of one pass: b'_j = Pi_fp16(sum num /
 // sum den) over the segments of column j's tile, added in segment order.
@@ -344,7 +333,7 @@ struct PassStats {
 enum : int { kPassPlain = 0, kPassStats = 1, kPassInit = 2 };
 
 template <int WT, int GRID, int AFMT, int G, int MODE>
-__global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
+__global__ void __launch_bounds__(kThreads, kPassOcc)
     bcd_pass_kernel(const void* __restrict__ W, const double* __restrict__ part_in, void* __restrict__ a_,
                     int32_t gM, int32_t gN, int32_t gldw, int32_t gS, int32_t gL, int32_t gtotal,
                     int32_t gn_tiles, int32_t gmax_seg, const uint16_t* __restrict__ b,
@@ -437,16 +426,6 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
 
     const float* lb = s_b + sub * LC;
     const float* lrb = s_rb + sub * LC;
-#if DQ_B_IN_REGS
-    float rb_b[LC], rb_rb[LC];
-#pragma unroll
-    for (int e = 0; e < LC; ++e) { rb_b[e] = lb[e]; rb_rb[e] = lrb[e]; }
-#define LB(e) rb_b[e]
-#define LRB(e) rb_rb[e]
-#else
-#define LB(e) lb[e]
-#define LRB(e) lrb[e]
-#endif
     double cn[LC], cd[LC];
 #pragma unroll
     for (int e = 0; e < LC; ++e) { cn[e] = 0.0; cd[e] = 0.0; }
@@ -525,39 +504,27 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
       double num[NB], den[NB];
       float q[LC];    // Q1 here; becomes Q2 below
       float wrb[LC];  // W / b (rounded), shared by both requantizations
-      // The sums of a block run in DQ_ROW_CHAINS interleaved partial sums
-      // (more independent float64 chains in flight), combined pairwise.
       auto row_sums = [&]() {
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-          double pn[DQ_ROW_CHAINS], pd[DQ_ROW_CHAINS];
-#pragma unroll
-          for (int c = 0; c < DQ_ROW_CHAINS; ++c) { pn[c] = 0.0; pd[c] = 0.0; }
+          num[bl] = 0.0;
+          den[bl] = 0.0;
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            const double R = (double)(q[e] * LB(e));  // exact product
-            pn[k % DQ_ROW_CHAINS] = __builtin_fma((double)w[e], R, pn[k % DQ_ROW_CHAINS]);
-            pd[k % DQ_ROW_CHAINS] = __builtin_fma(R, R, pd[k % DQ_ROW_CHAINS]);
+            const double R = (double)(q[e] * lb[e]);  // exact product
+            num[bl] = __builtin_fma((double)w[e], R, num[bl]);
+            den[bl] = __builtin_fma(R, R, den[bl]);
           }
-#pragma unroll
-          for (int span = 1; span < DQ_ROW_CHAINS; span <<= 1)
-#pragma unroll
-            for (int c = 0; c + span < DQ_ROW_CHAINS; c += 2 * span) {
-              pn[c] += pn[c + span];
-              pd[c] += pd[c + span];
-            }
-          num[bl] = pn[0];
-          den[bl] = pd[0];
         }
       };
       {
         float ra[NB], y[LC];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
-          ra[bl] = kExactQ ? recip_pow2(a_old[bl]) : __builtin_amdgcn_rcpf(a_old[bl]);
+          ra[bl] = recip_scale<AFMT>(a_old[bl]);
 #pragma unroll
-        for (int e = 0; e < LC; ++e) wrb[e] = w[e] * LRB(e);
+        for (int e = 0; e < LC; ++e) wrb[e] = w[e] * lrb[e];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -574,7 +541,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
               for (int k = 0; k < BL; ++k) {
                 const int e = bl * BL + k;
                 if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                  q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], LB(e));
+                  q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], lb[e]);
               }
           }
         }
@@ -590,7 +557,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
               const int e = bl * BL + k;
               // a Q b is exact in float64: q b is exact in float32
               const double wk = (double)w[e];
-              const double d = wk - (double)(q[e] * LB(e)) * (double)a_old[bl];
+              const double d = wk - (double)(q[e] * lb[e]) * (double)a_old[bl];
               st_sse = __builtin_fma(d, d, st_sse);
               st_w2 = __builtin_fma(wk, wk, st_w2);
             }
@@ -636,7 +603,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
         float y[LC];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
-          const float ra = kExactQ ? recip_pow2(a_new[bl]) : __builtin_amdgcn_rcpf(a_new[bl]);
+          const float ra = recip_scale<AFMT>(a_new[bl]);
 #pragma unroll
           for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra;
         }
@@ -651,7 +618,7 @@ __global__ void __launch_bounds__(kThreads, DQ_PASS_OCC)
               for (int k = 0; k < BL; ++k) {
                 const int e = bl * BL + k;
                 if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                  q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], LB(e));
+                  q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], lb[e]);
               }
           }
         }
@@ -792,7 +759,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
     raw.unpack(w);
 #pragma unroll
     for (int bl = 0; bl < NB; ++bl) {
-      const float ra = __builtin_amdgcn_rcpf(av[bl]);
+      const float ra = recip_scale<AFMT>(av[bl]);
 #pragma unroll
       for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
     }

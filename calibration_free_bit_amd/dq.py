@@ -130,8 +130,16 @@ def problem(rows: int, cols: int, fmt: Format, w_type: int, ldw: int | None = No
 
 def problem_for(W: torch.Tensor, fmt: Format) -> Problem:
     """dq_problem describing a 2-D weight tensor (float32, or bf16 given as
-    torch.bfloat16 or as its uint16 bit patterns in an int16 tensor)."""
-    w_type = W_F32 if W.dtype == torch.float32 else W_BF16
+    torch.bfloat16 or as its uint16 bit patterns in an int16 tensor) whose
+    rows are contiguous (any row pitch)."""
+    if W.dtype == torch.float32:
+        w_type = W_F32
+    elif W.dtype in (torch.bfloat16, torch.int16):
+        w_type = W_BF16
+    else:
+        raise TypeError(f"W must be float32, bfloat16 or int16 (bf16 bits), not {W.dtype}")
+    if W.dim() != 2 or (W.shape[1] > 1 and W.stride(1) != 1):
+        raise ValueError("W must be a 2-D tensor with contiguous rows (stride(1) == 1)")
     return problem(W.shape[0], W.shape[1], fmt, w_type, W.stride(0))
 
 
@@ -231,9 +239,14 @@ class Solver:
             bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stream=stream)
             return None
         need = stats_workspace_bytes(self.p)
-        if self.ws.numel() < need:
-            self.ws = torch.empty((need,), dtype=torch.uint8, device=self.W.device)
-        out = torch.zeros((n + 1, 3), dtype=torch.float64, device=self.W.device)
+        # allocate (and clear) on the stream the call runs on, so that the
+        # kernels are ordered after the fill
+        if isinstance(stream, int):
+            raise ValueError("iterate(stats=True) needs a torch stream (or None)")
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            if self.ws.numel() < need:
+                self.ws = torch.empty((need,), dtype=torch.uint8, device=self.W.device)
+            out = torch.zeros((n + 1, 3), dtype=torch.float64, device=self.W.device)
         bcd_iterate(self.p, self.W, self.a, self.b, n, self.ws, stats=out, stream=stream)
         return out
 

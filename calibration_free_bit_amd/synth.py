@@ -136,6 +136,12 @@ WORKLOADS = {
         "nvfp4_g16_4096x14336_bf16",
         MatrixSpec(4096, 14336, "normal", 0.01, 0.01, (25.0, 25.0), "bf16"),
         "nvfp4_g16", 20, (0, 1, 2)),
+    # the gate/up projection shape of the Llama-3.1-8B set, with the set's
+    # value recipe; seeds are the gate matrices of layers 0, 1 and 2
+    "int4_g64_14336x4096_bf16": Workload(
+        "int4_g64_14336x4096_bf16",
+        MatrixSpec(14336, 4096, "normal", 0.02, 0.01, (20.0, 20.0), "bf16"),
+        "int4_g64", 20, (4, 1004, 2004)),
     # the further MX formats, on the same 4096x4096 q_proj-shaped matrix
     "mxfp4_g32_4096x4096_bf16": Workload(
         "mxfp4_g32_4096x4096_bf16",

@@ -132,7 +132,7 @@ int dq_init_colnorm(const dq_problem* p, const void* W, void* a, uint16_t* b,
  * requantize; column update of b with S = D_a Q over all rows; requantize
  * (the last requantization is the next iteration's first step). The state
  * is exactly (a, b): iterate(k1) then iterate(k2) equals iterate(k1+k2).
- * n_iters = 0 is a no-op.
+ * n_iters = 0 leaves a and b as they are (with stats it writes row 0).
  *   W          in      [rows, ldw] of w_type
  *   a, b       in/out  as written by dq_init_rtn
  *   workspace  scratch of at least dq_workspace_bytes(p) bytes (with stats:

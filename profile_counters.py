@@ -1,22 +1,31 @@
 """Collect the rocprofv3 evidence behind bench.py's roofline entry.
 
-Runs, each in its own rocprofv3 process:
-  1. --kernel-trace --stats of ``bench.py`` (per-kernel average durations);
-  2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of ``bench.py`` (HBM bytes per
-     dispatch, in KiB), then --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_WAVES
-     (instructions issued by the profiled kernel: the BCD pass for a weight
-     workload, the activation quantizer for an ``act_`` workload);
-  3. the same two counters for ``bench.py --copy-calibration``, a plain
-     device copy of 256 MiB, whose known bytes give the scale factors of
-     the two counters.
-and writes to OUT_DIR (STEM: bcd_pass_<workload>, or act_quant_<...> for
-an activation workload act_<...>):
+For a single-matrix or activation workload W (stem bcd_pass_W, or
+act_quant_<...> for an activation workload act_<...>), each in its own
+rocprofv3 process:
+  1. --kernel-trace --stats of ``bench.py --workload W`` (per-kernel
+     average durations);
+  2. --pmc FETCH_SIZE, then --pmc WRITE_SIZE of the same command with 2
+     timed steps (HBM bytes per dispatch, in KiB), then --pmc SQ_INSTS_VALU
+     SQ_INSTS_SALU SQ_WAVES (instructions of the profiled kernel: the plain
+     BCD pass, or the activation quantizer);
+  3. the same two byte counters for ``bench.py --copy-calibration``, a plain
+     device copy of 256 MiB, whose known bytes give the counters' scale
+     factors;
+and writes to OUT_DIR:
   STEM_kernel_trace.md   kernel-trace summary
-  STEM_counters.json     traffic per launch + factors
+  STEM_counters.json     traffic and instructions per launch + factors
   STEM_counters.md       the same, readable
 
+For the Llama-3.1-8B set (the default workload) it writes the kernel trace
+of the default bench command (``bench.py`` with 2 timed steps), with the
+average of the pass launches bench.py times for its roofline entry (the
+last ones of the run: T passes at a time on the gate matrix), and collects
+1.-3. for the single-matrix workload of that shape,
+int4_g64_14336x4096_bf16 (the same matrix recipe; layer 0's gate seed).
+
 Usage (on a machine with the GPU; rocprofv3 on PATH):
-  python -m calibration_free_bit_amd.profile_counters OUT_DIR [--workload W]
+  python profile_counters.py OUT_DIR [--workload W]
 """
 
 from __future__ import annotations
@@ -30,8 +39,7 @@ import sys
 import tempfile
 from collections import defaultdict
 
-HERE = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(HERE)
+ROOT = os.path.dirname(os.path.abspath(__file__))
 BENCH = os.path.join(ROOT, "bench.py")
 
 
@@ -51,6 +59,7 @@ def _shown(cmd):
 
 
 def _rocprof(args, prog, tag, work, timeout=300):
+    """Run prog under rocprofv3; returns (output dir, shown command, stdout)."""
     out = os.path.join(work, tag)
     cmd = ["rocprofv3", *args, "-d", out, "-o", "run", "--output-format", "csv", "--",
            sys.executable, *prog]
@@ -60,7 +69,8 @@ def _rocprof(args, prog, tag, work, timeout=300):
     if r.returncode not in (0,):
         print(r.stdout[-2000:], r.stderr[-4000:], flush=True)
         raise RuntimeError(f"rocprofv3 failed ({r.returncode}) for {tag}")
-    return out, _shown(cmd)
+    print(f"[profile] {tag} done", flush=True)
+    return out, _shown(cmd), r.stdout
 
 
 def _find(root, suffix):
@@ -92,19 +102,41 @@ def _counters(root, counter, name_has):
     return [per[k] for k in sorted(per)]
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("out_dir")
-    ap.add_argument("--workload", default="int4_g64_4096x4096_bf16")
-    args = ap.parse_args()
-    os.makedirs(args.out_dir, exist_ok=True)
-    sys.path.insert(0, ROOT)
-    import bench  # for the source hash and the workload definition
-    from calibration_free_bit_amd import synth
+def _json_line(stdout: str):
+    for line in reversed(stdout.splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    raise RuntimeError("bench.py printed no JSON line")
 
-    from calibration_free_bit_amd import dq
-    if args.workload in synth.ACT_WORKLOADS:
-        aw = synth.ACT_WORKLOADS[args.workload]
+
+def _trace_table(tr, title, cmd):
+    stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
+    lines = [f"# Kernel trace: {title}", "", "Command:", "", f"    {cmd}", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} % |")
+    return lines
+
+
+def _dispatches(tr, name_has):
+    """(start, end) in ns of every dispatch of the kernel, in dispatch order."""
+    rows = []
+    for r in csv.DictReader(open(_find(tr, "kernel_trace.csv"))):
+        if _matches(r["Kernel_Name"], name_has):
+            rows.append((int(r["Dispatch_Id"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    return [(a, b) for _, a, b in rows]
+
+
+def profile_workload(name, out_dir, work):
+    """Kernel trace and counters of a single-matrix or activation workload."""
+    import bench  # for the source hash and the workload definitions
+    from calibration_free_bit_amd import dq, synth
+    if name in synth.ACT_WORKLOADS:
+        aw = synth.ACT_WORKLOADS[name]
         kernel, what = "act_quant_kernel", "activation quantization"
         launch, unit = "launch", "activation element"
         M, N = aw.tokens, aw.cols
@@ -112,51 +144,38 @@ def main():
         b_alg = bench.act_bytes_per_elem(fmt.code_bits, 2 if fmt.a_fmt == dq.SCALE_FP16 else 1,
                                          fmt.group, M)
     else:
-        wl = synth.WORKLOADS[args.workload]
+        wl = synth.WORKLOADS[name]
         kernel, what = "bcd_pass_kernel", "BCD solver"
         launch, unit = "pass launch", "weight element"
         M, N = wl.spec.rows, wl.spec.cols
         fmt = dq.FORMATS[wl.fmt]
         b_alg = bench.alg_bytes_per_elem(2 if wl.spec.dtype == "bf16" else 4,
                                          2 if fmt.a_fmt == dq.SCALE_FP16 else 1, fmt.group, M)
-    name = args.workload
     stem = bench.profile_stem(name)
     bench_args = [BENCH, "--workload", name, "--no-cpu-baseline"]
-    work = tempfile.mkdtemp(prefix="dqprof_", dir="/tmp")
 
     # 1. kernel trace
-    tr, tr_cmd = _rocprof(["--kernel-trace", "--stats"], bench_args,
-                          "trace", work)
-    stats = list(csv.DictReader(open(_find(tr, "kernel_stats.csv"))))
-    lines = [f"# Kernel trace: {what}, workload {name}", "",
-             "Command:", "", f"    {tr_cmd}", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share |",
-             "|---|---:|---:|---:|---:|---:|"]
-    for r in stats:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.1f} % |")
-    open(os.path.join(args.out_dir, f"{stem}_kernel_trace.md"), "w").write(
-        "\n".join(lines) + "\n")
+    tr, tr_cmd, _ = _rocprof(["--kernel-trace", "--stats"], bench_args, f"{stem}_trace", work)
+    lines = _trace_table(tr, f"{what}, workload {name}", tr_cmd)
+    open(os.path.join(out_dir, f"{stem}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
 
     # 2./3. byte counters, each counter in its own run
     res = {}
     cmds = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        d, c = _rocprof(["--pmc", counter], bench_args + ["--steps", "2", "--warmup", "1"],
-                        f"pass_{counter}", work, timeout=180)
+        d, c, _ = _rocprof(["--pmc", counter], bench_args + ["--steps", "2", "--warmup", "1"],
+                           f"{stem}_{counter}", work, timeout=180)
         res[("pass", counter)] = _counters(d, counter, kernel)
         cmds[("pass", counter)] = c
-        d, c = _rocprof(["--pmc", counter], [BENCH, "--copy-calibration"], f"copy_{counter}", work,
-                        timeout=180)
-        vals = _counters(d, counter, "")
-        res[("copy", counter)] = vals
+        d, c, _ = _rocprof(["--pmc", counter], [BENCH, "--copy-calibration"], f"copy_{counter}", work,
+                           timeout=180)
+        res[("copy", counter)] = _counters(d, counter, "")
         cmds[("copy", counter)] = c
 
     # 4. VALU instruction count of the kernel (wave-level instructions;
     #    x64 lanes = lane operations), for its VALU roofline
-    d, c = _rocprof(["--pmc", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAVES"],
-                    bench_args + ["--steps", "2", "--warmup", "1"], "pass_valu", work, timeout=180)
+    d, c, _ = _rocprof(["--pmc", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_WAVES"],
+                       bench_args + ["--steps", "2", "--warmup", "1"], f"{stem}_valu", work, timeout=180)
     valu = _counters(d, "SQ_INSTS_VALU", kernel)
     salu = _counters(d, "SQ_INSTS_SALU", kernel)
     waves = _counters(d, "SQ_WAVES", kernel)
@@ -187,13 +206,14 @@ def main():
         "write_factor": write_factor,
         "traffic_bytes_per_launch": traffic,
         "traffic_bytes_per_element": traffic / (M * N),
+        "alg_bytes_per_element": b_alg,
         "valu_insts_per_launch": sum(valu) / len(valu),
         "salu_insts_per_launch": sum(salu) / len(salu),
         "waves_per_launch": sum(waves) / len(waves),
         "valu_lane_ops_per_element": 64.0 * sum(valu) / len(valu) / (M * N),
         "commands": {f"{k[0]}_{k[1]}": v for k, v in cmds.items()},
     }
-    json.dump(rec, open(os.path.join(args.out_dir, f"{stem}_counters.json"), "w"), indent=2)
+    json.dump(rec, open(os.path.join(out_dir, f"{stem}_counters.json"), "w"), indent=2)
     md = [f"# HBM byte counters: {kernel}, workload {name}", "",
           f"Per {launch} (average of {len(pf)} dispatches): FETCH_SIZE {fetch_kib:.0f} KiB, "
           f"WRITE_SIZE {write_kib:.0f} KiB.", "",
@@ -201,14 +221,54 @@ def main():
           f"WRITE_SIZE {w_copy / 1024:.0f} KiB, so the factors are {fetch_factor:.4f} (fetch) and "
           f"{write_factor:.4f} (write).", "",
           f"Traffic per launch: {traffic / 1e6:.2f} MB = {traffic / (M * N):.3f} bytes per {unit} "
-          f"(algorithmic: {b_alg:.4f}).", "",
+          f"(algorithmic: {b_alg:.4f}, ratio {traffic / (M * N) / b_alg:.3f}).", "",
           f"VALU: {rec['valu_insts_per_launch']:.4g} wave instructions per launch "
           f"({rec['valu_lane_ops_per_element']:.2f} lane operations per {unit}), "
           f"SALU {rec['salu_insts_per_launch']:.4g}, waves {rec['waves_per_launch']:.0f}.", "",
           "Commands:", ""]
     md += [f"    {v}" for v in cmds.values()]
-    open(os.path.join(args.out_dir, f"{stem}_counters.md"), "w").write("\n".join(md) + "\n")
-    print(json.dumps(rec, indent=1))
+    open(os.path.join(out_dir, f"{stem}_counters.md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps(rec, indent=1), flush=True)
+
+
+def profile_set(out_dir, work):
+    """Kernel trace of the default bench command (the Llama-3.1-8B set),
+    with the average of the pass launches its roofline entry times."""
+    import bench
+    stem = bench.profile_stem(bench.SET_WORKLOAD)
+    tr, tr_cmd, stdout = _rocprof(["--kernel-trace", "--stats"],
+                                  [BENCH, "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+                                  f"{stem}_trace", work, timeout=600)
+    res = _json_line(stdout)
+    n = res["roofline"]["launches"]
+    d = _dispatches(tr, "bcd_pass_kernel")[-n:]
+    avg_us = sum(b - a for a, b in d) / len(d) / 1e3
+    lines = _trace_table(tr, f"BCD solver, the Llama-3.1-8B set ({bench.SET_WORKLOAD})", tr_cmd)
+    lines += ["", f"Roofline launches (the last {n} plain pass launches of the run: T passes at a "
+                  f"time on layer 0's gate matrix, 14336x4096, alone on one stream): average "
+                  f"{avg_us:.2f} us in this trace; bench.py measured {res['roofline']['avg_launch_us']:.2f} us "
+                  f"with events in the same run (its average includes one final column update per "
+                  f"T passes).", "",
+              f"Whole step: {res['ms_per_step']:.2f} ms, {res['value'] / 1e12:.3f} T elements/s per "
+              f"iteration (under the profiler)."]
+    open(os.path.join(out_dir, f"{stem}_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines[-3:]), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("out_dir")
+    ap.add_argument("--workload", default=None, help="default: the Llama-3.1-8B set")
+    args = ap.parse_args()
+    os.makedirs(args.out_dir, exist_ok=True)
+    sys.path.insert(0, ROOT)
+    import bench
+    work = tempfile.mkdtemp(prefix="dqprof_", dir="/tmp")
+    if args.workload in (None, bench.SET_WORKLOAD):
+        profile_set(args.out_dir, work)
+        profile_workload("int4_g64_14336x4096_bf16", args.out_dir, work)
+    else:
+        profile_workload(args.workload, args.out_dir, work)
 
 
 if __name__ == "__main__":

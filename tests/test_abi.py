@@ -150,8 +150,10 @@ def test_iterate_checks_workspace_and_stats_before_launch():
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need_st - 1, ok, None) == dq.ERR_WORKSPACE
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 1, ok, need_st, ctypes.c_void_p(260),
                             None) == dq.ERR_INVALID_ARG
-    # zero iterations is a no-op that touches nothing
+    # zero iterations is a no-op that touches nothing; with statistics it
+    # writes row 0, so it needs the workspace
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 0, None, 0, None, None) == dq.OK
+    assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 0, None, 0, ok, None) == dq.ERR_WORKSPACE
 
 
 def test_solve_checks_arguments_before_launch():

@@ -101,6 +101,62 @@ def test_rows_spanning_many_binades(name):
     _check(data, fmt, 4, f"{name} rows over 40 binades")
 
 
+def _range_matrix(rows_big, rows_small, N, big, small, seed):
+    """Normal rows (std 0.02), rows_big rows of std `big`, and rows_small
+    rows whose magnitudes lie in [1, 1.75) * small with random signs (all
+    normal bf16 values)."""
+    rng = np.random.default_rng(seed)
+    W = rng.normal(0, 0.02, (rows_big + rows_small + 16, N))
+    W[:rows_big] = rng.normal(0, 1.0, (rows_big, N)) * big
+    mag = rng.uniform(1.0, 1.75, (rows_small, N)) * rng.choice([-1.0, 1.0], (rows_small, N))
+    W[rows_big:rows_big + rows_small] = mag * small
+    return synth.bf16_bits(W)
+
+
+# (format, rows of std big, rows near small, the range ends the oracle's
+# result must reach: (which scale, value))
+RANGE_CASES = {
+    # fp16 block and column scales saturating at 65504 (and the fp16 floor
+    # 2^-24 at the start, for the normal rows)
+    "fp16_saturates": ("int4_g64", 8, 0, 1e12, 0.0, (("a", 65504.0),)),
+    # blocks of about 2^-24 with non-zero codes: the fp16 floor
+    "fp16_floor": ("int4_g64", 0, 8, 1.0, 2.0 ** -24, (("a", 2.0 ** -24),)),
+    # E4M3 block scales at 448 and, at the start, at 2^-9
+    "e4m3_ends": ("nvfp4_g16", 8, 8, 1e4, 2.0 ** -14, (("a", 448.0),)),
+    # E8M0 block scales at 2^-127 (a float32 subnormal)
+    "e8m0_floor_mxint4": ("mxint4_g32", 0, 8, 1.0, 2.0 ** -125, (("a", 2.0 ** -127),)),
+    "e8m0_floor_mxfp8": ("mxfp8_g32", 0, 8, 1.0, 2.0 ** -125, (("a", 2.0 ** -127),)),
+    "e8m0_floor_mxfp4": ("mxfp4_g32", 0, 8, 1.0, 2.0 ** -125, (("a", 2.0 ** -127),)),
+}
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+@pytest.mark.parametrize("case", sorted(RANGE_CASES))
+def test_projection_range_ends(case, iters):
+    """Block and column scales at the ends of their legal sets (saturation
+    at the largest value, the smallest legal value), through init, the
+    iterations and packing, and through dq_solve: bit-identical to the
+    oracle."""
+    name, nb, ns, big, small, ends = RANGE_CASES[case]
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    data = _range_matrix(nb, ns, 256, big, small, 5)
+    W64 = as_f64(data)
+    sol = D.solve(W64, ofmt, iters)
+    for which, v in ends:
+        assert np.any((sol.a if which == "a" else sol.b) == v), (case, which, v)
+    if case == "fp16_saturates" and iters > 0:
+        assert np.any(sol.b == 65504.0)
+    print(f"[case] range ends {case} T={iters}", flush=True)
+    g = DeviceRun(data, fmt).run(iters)
+    r = compare(W64, g.a, g.b, g.Q, sol, ofmt, f"{case} T={iters}")
+    assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
+    np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, ofmt))
+    h = DeviceRun(data, fmt).solve(iters)
+    assert np.array_equal(h.a, g.a) and np.array_equal(h.b, g.b)
+    np.testing.assert_array_equal(h.packed, g.packed)
+
+
 @pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32", "mxfp8_g32"])
 def test_exact_ties_power_of_two_scales(name):
     # E8M0 block scales with b = 1 put many W / a exactly on grid midpoints
@@ -562,20 +618,28 @@ def test_activation_rescale_quantize(name, tokens):
 # ------------------------------------------------------------ full-size workloads
 
 FULL = ["int4_g64_4096x4096_bf16", "mxint4_g32_14336x4096_bf16", "nvfp4_g16_4096x14336_bf16",
-        "mxfp4_g32_4096x4096_bf16", "mxint8_g32_4096x4096_bf16", "mxfp8_g32_4096x4096_bf16"]
+        "int4_g64_14336x4096_bf16", "mxfp4_g32_4096x4096_bf16", "mxint8_g32_4096x4096_bf16",
+        "mxfp8_g32_4096x4096_bf16"]
 
 
-@pytest.mark.parametrize("wl_name", FULL)
-def test_full_size_sampled_stripes(wl_name):
+FULL_SEEDS = [(w, s) for w in FULL for s in synth.WORKLOADS[w].seeds[:1]] + \
+    [(w, s) for w in ("int4_g64_4096x4096_bf16", "mxint4_g32_14336x4096_bf16",
+                      "nvfp4_g16_4096x14336_bf16", "int4_g64_14336x4096_bf16")
+     for s in synth.WORKLOADS[w].seeds[1:]]
+
+
+@pytest.mark.parametrize("wl_name,seed", FULL_SEEDS)
+def test_full_size_sampled_stripes(wl_name, seed):
     """The benchmarked configurations at full size, in the launch
     configuration the benchmark times (one dq_solve per step), checked on
-    whole column stripes; the separate init / iterate / pack calls must
-    give the same bits."""
+    16 whole column stripes (both ends, the stripes of the first and last
+    outlier column, and random ones); the separate init / iterate / pack
+    calls must give the same bits."""
     wl = synth.WORKLOADS[wl_name]
     fmt = dq.FORMATS[wl.fmt]
     ofmt = oracle_fmt(fmt)
-    m = synth.make_matrix(wl.spec, wl.seeds[0])
-    print(f"[case] {wl_name} full solve T={wl.iters}", flush=True)
+    m = synth.make_matrix(wl.spec, seed)
+    print(f"[case] {wl_name} seed {seed} full solve T={wl.iters}", flush=True)
     g = DeviceRun(m.data, fmt).solve(wl.iters)
     sep = DeviceRun(m.data, fmt).run(wl.iters)
     assert torch.equal(g.s.a, sep.s.a) and torch.equal(g.s.b, sep.s.b)
@@ -584,9 +648,10 @@ def test_full_size_sampled_stripes(wl_name):
     a, b, Q = g.a, g.b, g.Q
     G = fmt.group
     n_str = m.spec.cols // G
-    rng = np.random.default_rng(0)
-    stripes = sorted({0, n_str - 1, int(m.outlier_cols[0]) // G, int(m.outlier_cols[-1]) // G,
-                      *rng.choice(n_str, 3, replace=False).tolist()})
+    rng = np.random.default_rng(seed)
+    stripes = {0, n_str - 1, int(m.outlier_cols[0]) // G, int(m.outlier_cols[-1]) // G}
+    stripes = sorted(stripes | set(rng.choice(sorted(set(range(n_str)) - stripes), 16 - len(stripes),
+                                              replace=False).tolist()))
     W64_cols = synth.bf16_to_f64(m.data[:, np.concatenate([np.arange(s * G, s * G + G) for s in stripes])])
     for k, s in enumerate(stripes):
         Ws = W64_cols[:, k * G:(k + 1) * G]
