@@ -89,6 +89,41 @@ Workspace pass_geometry(const dq_problem* p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DQ_OK : DQ_ERR_HIP; }
 
+// Calls f.template operator()<WT, GRID, AFMT, G>() for p's format.
+template <class F>
+int dispatch(const dq_problem& p, F&& f) {
+  auto by_group = [&]<int WT, int GR, int AF>() -> int {
+    switch (p.group) {
+      case 16: return f.template operator()<WT, GR, AF, 16>();
+      case 32: return f.template operator()<WT, GR, AF, 32>();
+      case 64: return f.template operator()<WT, GR, AF, 64>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  auto by_afmt = [&]<int WT, int GR>() -> int {
+    switch (p.a_fmt) {
+      case DQ_SCALE_FP16: return by_group.template operator()<WT, GR, dq::kScaleFp16>();
+      case DQ_SCALE_E8M0: return by_group.template operator()<WT, GR, dq::kScaleE8M0>();
+      case DQ_SCALE_E4M3: return by_group.template operator()<WT, GR, dq::kScaleE4M3>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  auto by_grid = [&]<int WT>() -> int {
+    switch (p.grid) {
+      case DQ_GRID_INT4: return by_afmt.template operator()<WT, dq::kGridInt4>();
+      case DQ_GRID_E2M1: return by_afmt.template operator()<WT, dq::kGridE2M1>();
+      case DQ_GRID_INT8: return by_afmt.template operator()<WT, dq::kGridInt8>();
+      case DQ_GRID_E4M3: return by_afmt.template operator()<WT, dq::kGridE4M3>();
+    }
+    return DQ_ERR_UNSUPPORTED;
+  };
+  switch (p.w_type) {
+    case DQ_W_F32: return by_grid.template operator()<dq::kWF32>();
+    case DQ_W_BF16: return by_grid.template operator()<dq::kWBF16>();
+  }
+  return DQ_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" {
