@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "dq.h"
 #include "dq_device.h"
@@ -88,6 +89,30 @@ Workspace pass_geometry(const dq_problem* p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DQ_OK : DQ_ERR_HIP; }
+
+// Scratch of dq_bcd_iterate_noalloc: the two alternating buffers of partial
+// column sums, in a fixed array that every GPU the library runs on holds
+// for the life of the process. Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) unsigned char scratch[DQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or nullptr on failure.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 // Calls f.template operator()<WT, GRID, AFMT, G>() for p's format.
 template <class F>
@@ -196,6 +221,23 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
                                                          nullptr, stats, its.part, st));
     return hip_status(
         dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, false, st));
+  });
+}
+
+int dq_bcd_iterate_noalloc(const dq_problem* p, const void* W, void* a, uint16_t* b, int32_t n_iters,
+                           void* stream) {
+  if (int s = check_problem(p)) return s;
+  if (!W || !a || !b || !aligned16(W) || n_iters < 0) return DQ_ERR_INVALID_ARG;
+  const Workspace ws = pass_geometry(p);
+  if (ws.pass_bytes > DQ_NOALLOC_SCRATCH_BYTES) return DQ_ERR_WORKSPACE;
+  if (n_iters == 0) return DQ_OK;
+  // every pass writes its partials before the next one reads them and the
+  // first pass reads none, so the scratch needs no clearing
+  double* part = static_cast<double*>(scratch_address());
+  if (!part) return DQ_ERR_HIP;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
+    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, false, st));
   });
 }
 

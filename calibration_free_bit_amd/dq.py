@@ -25,7 +25,7 @@ SCALE_FP16, SCALE_E8M0, SCALE_E4M3 = 0, 1, 2
 W_F32, W_BF16 = 0, 1
 
 EXPORTS = ("dq_workspace_bytes", "dq_stats_workspace_bytes", "dq_init_rtn", "dq_init_colnorm",
-           "dq_bcd_iterate", "dq_solve", "dq_pack_codes", "dq_quant_report", "dq_rescale_quantize_act",
+           "dq_bcd_iterate", "dq_bcd_iterate_noalloc", "dq_solve", "dq_pack_codes", "dq_quant_report", "dq_rescale_quantize_act",
            "dq_status_string", "dq_abi_version")
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.dq_init_colnorm.restype = ctypes.c_int
         L.dq_bcd_iterate.argtypes = [P, vp, vp, vp, i32, vp, sz, vp, vp]
         L.dq_bcd_iterate.restype = ctypes.c_int
+        L.dq_bcd_iterate_noalloc.argtypes = [P, vp, vp, vp, i32, vp]
+        L.dq_bcd_iterate_noalloc.restype = ctypes.c_int
         L.dq_solve.argtypes, L.dq_solve.restype = [P, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int
         L.dq_pack_codes.argtypes, L.dq_pack_codes.restype = [P, vp, vp, vp, vp, vp], ctypes.c_int
         L.dq_quant_report.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -168,6 +170,11 @@ def bcd_iterate(p: Problem, W, a, b, n_iters: int, workspace, workspace_nbytes: 
     _check("dq_bcd_iterate", lib().dq_bcd_iterate(
         ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), int(n_iters), _ptr(workspace), int(nbytes),
         _ptr(stats), _stream(stream)))
+
+
+def bcd_iterate_noalloc(p: Problem, W, a, b, n_iters: int, stream=None) -> None:
+    _check("dq_bcd_iterate_noalloc", lib().dq_bcd_iterate_noalloc(
+        ctypes.byref(p), _ptr(W), _ptr(a), _ptr(b), int(n_iters), _stream(stream)))
 
 
 def solve(p: Problem, W, a, b, n_iters: int, packed, workspace, workspace_nbytes: int | None = None,

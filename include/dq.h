@@ -154,6 +154,25 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b,
                    int32_t n_iters, void* workspace, size_t workspace_bytes,
                    double* stats, void* stream);
 
+/* dq_bcd_iterate for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same iterations, with a, b and every bit of the result
+ * as dq_bcd_iterate (stats = NULL) leaves them, but with no workspace
+ * argument. The partial column sums live in a fixed array inside the
+ * library of DQ_NOALLOC_SCRATCH_BYTES bytes, which each GPU the library
+ * runs on holds until the process ends; nothing is allocated or freed.
+ *   W, a, b, n_iters, stream  as for dq_bcd_iterate
+ * Returns DQ_ERR_WORKSPACE when the problem's partial sums need more than
+ * DQ_NOALLOC_SCRATCH_BYTES (dq_workspace_bytes(p) <= that bound always
+ * fits), and DQ_ERR_HIP if the array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array, so calls that may overlap
+ * on one GPU (on different streams) race and must not be issued; calls on
+ * one stream are ordered and safe. The array keeps the last call's partial
+ * sums; no call depends on its earlier contents. */
+#define DQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dq_bcd_iterate_noalloc(const dq_problem* p, const void* W, void* a, uint16_t* b,
+                           int32_t n_iters, void* stream);
+
 /* The whole solve in one call: dq_init_rtn, dq_bcd_iterate(n_iters) and
  * dq_pack_codes, with a, b and packed exactly as those three calls leave
  * them. The absmax initialization is formed inside the first iteration's

@@ -156,6 +156,24 @@ def test_iterate_checks_workspace_and_stats_before_launch():
     assert L.dq_bcd_iterate(ctypes.byref(p), ok, ok, ok, 0, None, 0, ok, None) == dq.ERR_WORKSPACE
 
 
+def test_noalloc_iterate_checks_arguments_before_launch():
+    L = dq.lib()
+    p = _p()
+    ok = ctypes.c_void_p(256)
+    f = L.dq_bcd_iterate_noalloc
+    assert f(ctypes.byref(p), None, ok, ok, 1, None) == dq.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), ok, None, ok, 1, None) == dq.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), ctypes.c_void_p(264), ok, ok, 1, None) == dq.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), ok, ok, ok, -1, None) == dq.ERR_INVALID_ARG
+    assert f(ctypes.byref(_p(cols=100)), ok, ok, ok, 1, None) == dq.ERR_SHAPE
+    # partial sums larger than the library's fixed scratch (16 MiB)
+    big = dq.problem(64, 1 << 20, dq.FORMATS["int4_g64"], dq.W_BF16)
+    assert L.dq_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    assert f(ctypes.byref(big), ok, ok, ok, 1, None) == dq.ERR_WORKSPACE
+    # zero iterations touch nothing
+    assert f(ctypes.byref(p), ok, ok, ok, 0, None) == dq.OK
+
+
 def test_solve_checks_arguments_before_launch():
     L = dq.lib()
     p = _p()
