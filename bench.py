@@ -13,8 +13,8 @@ for the dominant kernel, the BCD pass, on the dominant shape (gate/up,
 14336 x 4096, 54 % of the set's elements): its algorithmic bytes per
 launch (one read of W plus a read and a write of the block scales and the
 column scales) over its average duration, measured in this run with events
-on the stream it runs on, T passes at a time on one resident gate matrix
-after the timed steps. cpu_baseline times the float64 oracle (test
+on the stream it runs on, around the T passes of solves of one resident
+gate matrix after the timed steps. cpu_baseline times the float64 oracle (test
 infrastructure, never on the product path) on the whole of layer 0 with a
 pool of worker processes.
 
@@ -255,21 +255,22 @@ def run_set(args):
     b_step = alg_bytes_per_elem(2, 2, fmt.group, 4096)
     step_gbs = value * b_step / 1e9  # whole step, start and packing included
 
-    # the dominant kernel on the dominant shape: T passes at a time of layer
-    # 0's gate matrix (14336 x 4096), alone on the current stream, timed with
-    # events on that stream (each T includes one final column update)
+    # the dominant kernel on the dominant shape: the T passes of a solve of
+    # layer 0's gate matrix (14336 x 4096) from the absmax start, alone on
+    # the current stream, timed with events on that stream around
+    # dq_bcd_iterate(T) (each T includes one final column update)
     gate = solvers[[k for k, it in enumerate(items) if it[2] == "gate"][0]]
     M, N = gate.W.shape
     reps = max(3, args.steps)
-    gate.iterate(T)  # warm
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record(cur)
-    for _ in range(reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r0, r1 in ev:
+        gate.init()
+        r0.record(cur)
         gate.iterate(T)
-    r1.record(cur)
+        r1.record(cur)
     torch.cuda.synchronize()
-    pass_s = r0.elapsed_time(r1) * 1e-3 / (reps * T)
+    pass_s = sum(r0.elapsed_time(r1) for r0, r1 in ev) * 1e-3 / (reps * T)
     b_pass = alg_bytes_per_elem(2, 2, fmt.group, M)
     achieved = b_pass * M * N / pass_s / 1e9
     dom = f"int4_g64_{M}x{N}_bf16"

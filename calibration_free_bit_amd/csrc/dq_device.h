@@ -137,24 +137,22 @@ __device__ __forceinline__ double ls_scale(double num, double den) {
   return den > 0.0 ? project<AFMT>(num / den) : 1.0;
 }
 
-// Fast path of ls_scale, in float32. The quotient num/den is formed from
-// the float32 roundings of num and den and a 1-ulp reciprocal, so it is
-// within 5 * 2^-24 (relative) of the exact quotient. For fp16 and E4M3 the
+// Certified projection of a float32 estimate of a positive quotient.
+// nf / df must be within relative error eps / 1.25 of the exact quotient,
+// counting the 1-ulp reciprocal and the product formed here (2^-24 each,
+// relative). Operands below 2^-100 are refused, so subnormal roundings
+// inside the estimate stay far below that bound. For fp16 and E4M3 the
 // hardware conversions (round to nearest even, subnormals kept) project
-// both ends of [x (1 - 2^-20), x (1 + 2^-20)], which contains the exact
+// both ends of [x (1 - eps), x (1 + eps)], which contains the exact
 // (clamped) quotient; rounding is monotone, so equal results at both ends
 // are the projection of the exact quotient. For E8M0 the quotient is
 // compared with the nearest binade midpoint. Otherwise `unsure` is set and
 // the caller must use ls_scale.
-constexpr float kScaleSure = 0x1p-20f;
-
 template <int AFMT>
-__device__ __forceinline__ float ls_scale_fast(double num, double den, bool& unsure) {
-  if (!(den > 0.0)) return 1.0f;
-  const float nf = (float)num, df = (float)den;
+__device__ __forceinline__ float project_certified(float nf, float df, float eps, bool& unsure) {
   const float qf = nf * __builtin_amdgcn_rcpf(df);
-  // far outside every format's range, or denormal operands: exact path
-  if (!(qf > 0x1p-100f && qf < 0x1p100f) || !(df > 0x1p-100f)) {
+  // far outside every format's range, or tiny operands: exact path
+  if (!(qf > 0x1p-100f && qf < 0x1p100f) || !(df > 0x1p-100f) || !(nf > 0x1p-100f)) {
     unsure = true;
     return 1.0f;
   }
@@ -162,22 +160,33 @@ __device__ __forceinline__ float ls_scale_fast(double num, double den, bool& uns
     const float x = __builtin_fmaxf(qf, 0x1p-127f);
     const int k = __builtin_amdgcn_frexp_expf(x) - 1;           // 2^k <= x < 2^(k+1)
     const float mid = __builtin_ldexpf(1.5f, k);
-    unsure |= __builtin_fabsf(x - mid) <= kScaleSure * x;
+    unsure |= __builtin_fabsf(x - mid) <= eps * x;
     return __builtin_ldexpf(1.0f, min(x >= mid ? k + 1 : k, 127));
   } else if constexpr (AFMT == kScaleFp16) {
     const float x = __builtin_amdgcn_fmed3f(qf, 0x1p-24f, 65504.0f);
-    const _Float16 rl = (_Float16)(x * (1.0f - kScaleSure));
-    const _Float16 rh = (_Float16)(x * (1.0f + kScaleSure));
+    const _Float16 rl = (_Float16)(x * (1.0f - eps));
+    const _Float16 rh = (_Float16)(x * (1.0f + eps));
     unsure |= __builtin_bit_cast(uint16_t, rl) != __builtin_bit_cast(uint16_t, rh);
     return (float)rl;
   } else {
     // OCP E4M3FN conversion of both ends into bytes 0 and 1 (the upper end
     // stays below 464, where the conversion would give NaN)
     const float x = __builtin_amdgcn_fmed3f(qf, 0x1p-9f, 448.0f);
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x * (1.0f - kScaleSure), x * (1.0f + kScaleSure), 0, false);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x * (1.0f - eps), x * (1.0f + eps), 0, false);
     unsure |= ((w ^ (w >> 8)) & 0xFF) != 0;
     return __builtin_amdgcn_cvt_f32_fp8(w, 0);
   }
+}
+
+// Fast path of ls_scale from float64 sums: the quotient of their float32
+// roundings with a 1-ulp reciprocal is within 5 * 2^-24 (relative) of the
+// exact quotient, inside the bracket of 2^-20.
+constexpr float kScaleSure = 0x1p-20f;
+
+template <int AFMT>
+__device__ __forceinline__ float ls_scale_fast(double num, double den, bool& unsure) {
+  if (!(den > 0.0)) return 1.0f;
+  return project_certified<AFMT>((float)num, (float)den, kScaleSure, unsure);
 }
 
 // ------------------------------------------------------- element quantizer

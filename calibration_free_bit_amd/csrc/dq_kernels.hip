@@ -40,19 +40,16 @@
 
 namespace dq {
 
-// Hide a value from the optimizer so that work derived from it is redone
-// where it is needed instead of being kept live in registers.
-template <class T>
-__device__ __forceinline__ void opaque(T& v) {
-  asm volatile("" : "+v"(v));
-}
-
 __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
 // The value of lane (lane ^ M) within each quad of lanes (M = 1 or 2), by a
-// DPP quad permutation (VALU moves instead of an LDS round trip).
+// DPP quad permutation (VALU moves instead of an LDS round trip). Every
+// source lane of a quad permutation exists, so bound_ctrl (zero for a
+// missing source) never applies; setting it lets the compiler fold the
+// float32 move into the add that consumes it. Called with every lane of
+// the wave active.
 template <int M>
 __device__ __forceinline__ double quad_xor(double v) {
   static_assert(M == 1 || M == 2, "quad permutations");
@@ -65,12 +62,12 @@ template <int M>
 __device__ __forceinline__ float quad_xor(float v) {
   static_assert(M == 1 || M == 2, "quad permutations");
   constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, true));
 }
 // The value of lane 7 - (lane & 7) within each group of 8 lanes (DPP
 // row_half_mirror): pairs every lane of one quad with one of the other.
 __device__ __forceinline__ float half_mirror(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
 }
 __device__ __forceinline__ double half_mirror(double v) {
   const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), 0x141, 0xF, 0xF, false);
@@ -250,6 +247,7 @@ __global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__
 // ------------------------------------------------------------ BCD pass
 
 constexpr int kThreads = 256;  // 4 waves
+constexpr float kRowSure = 0x1p-19f;  // bracket of the float32 row sums (32 units of 2^-24)
 constexpr int kPrefetch = 1;   // row steps in flight per lane
 constexpr int kPassOcc = 2;    // workgroups per CU the register budget must allow
 
@@ -501,10 +499,39 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
       // Q1 = q(W / (a b)) with the current state, fused with the row/block
       // least-squares sums (R = Q1 D_b). If any element of the wave lies
       // near a rounding midpoint the sums are redone with exact codes.
-      double num[NB], den[NB];
       float q[LC];    // Q1 here; becomes Q2 below
       float wrb[LC];  // W / b (rounded), shared by both requantizations
-      auto row_sums = [&]() {
+      // Row least-squares sums, first in float32 in two interleaved chains
+      // per lane. Every term W R and R^2 is non-negative (a non-zero code
+      // has the sign of its weight), so each fused multiply-add adds at most
+      // one rounding of a partial sum no larger than the whole sum: at most
+      // 8 units of 2^-24 (relative) per chain, one for joining the chains
+      // and one per join across the lanes of a block (two for G = 64), 11
+      // for the numerator and the denominator alike. Their quotient with a
+      // 1-ulp reciprocal is then within 25 units, inside the certified
+      // projection's bracket of kRowSure = 32 units. A wave with a block
+      // the bracket cannot decide redoes its sums in float64, where every
+      // product is exact.
+      float numf[NB], denf[NB];
+      auto row_sums_f32 = [&]() {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl) {
+          float n0 = 0.0f, n1 = 0.0f, d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+          for (int k = 0; k < BL; k += 2) {
+            const int e = bl * BL + k;
+            const float R0 = q[e] * lb[e], R1 = q[e + 1] * lb[e + 1];  // exact products
+            n0 = __builtin_fmaf(w[e], R0, n0);
+            d0 = __builtin_fmaf(R0, R0, d0);
+            n1 = __builtin_fmaf(w[e + 1], R1, n1);
+            d1 = __builtin_fmaf(R1, R1, d1);
+          }
+          numf[bl] = n0 + n1;
+          denf[bl] = d0 + d1;
+        }
+      };
+      double num[NB], den[NB];
+      auto row_sums_f64 = [&]() {
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) {
           num[bl] = 0.0;
@@ -545,7 +572,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
               }
           }
         }
-        row_sums();
+        row_sums_f32();
       }
       if constexpr (STATS) {
         // the state (a, b) this pass starts from, with its codes Q1
@@ -573,20 +600,32 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
       // blocks wider than a lane: the lanes of a block form (part of) a quad
       static_assert(LPB <= 4 && LPR == 4, "a block's lanes lie in one quad");
       if constexpr (LPB >= 2) {
-        num[0] += quad_xor<1>(num[0]);
-        den[0] += quad_xor<1>(den[0]);
+        numf[0] += quad_xor<1>(numf[0]);
+        denf[0] += quad_xor<1>(denf[0]);
       }
       if constexpr (LPB >= 4) {
-        num[0] += quad_xor<2>(num[0]);
-        den[0] += quad_xor<2>(den[0]);
+        numf[0] += quad_xor<2>(numf[0]);
+        denf[0] += quad_xor<2>(denf[0]);
       }
 
-      // project, synchronize the copy that assigns codes, store
+      // project, synchronize the copy that assigns codes, store. The
+      // float32 denominator is 0 exactly when every code of the block is 0
+      // (a non-zero R^2 is at least 2^-66, a normal float32).
       float a_new[NB];
       bool unsure = false;
 #pragma unroll
-      for (int bl = 0; bl < NB; ++bl) a_new[bl] = ls_scale_fast<AFMT>(num[bl], den[bl], unsure);
+      for (int bl = 0; bl < NB; ++bl)
+        a_new[bl] = denf[bl] > 0.0f ? project_certified<AFMT>(numf[bl], denf[bl], kRowSure, unsure) : 1.0f;
       if (wave_any(unsure)) {
+        row_sums_f64();
+        if constexpr (LPB >= 2) {
+          num[0] += quad_xor<1>(num[0]);
+          den[0] += quad_xor<1>(den[0]);
+        }
+        if constexpr (LPB >= 4) {
+          num[0] += quad_xor<2>(num[0]);
+          den[0] += quad_xor<2>(den[0]);
+        }
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) a_new[bl] = (float)ls_scale<AFMT>(num[bl], den[bl]);
       }
@@ -624,13 +663,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         }
       }
 
-      // column least-squares sums, S = D_a' Q2. The float64 copies of w made
-      // for the row sums stay live for bf16 weights; float32 weights need
-      // more registers, so there w is converted again.
-      if constexpr (WT == kWF32) {
-#pragma unroll
-        for (int e = 0; e < LC; ++e) opaque(w[e]);
-      }
+      // column least-squares sums in float64, S = D_a' Q2
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) {
 #pragma unroll

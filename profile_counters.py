@@ -244,8 +244,8 @@ def profile_set(out_dir, work):
     d = _dispatches(tr, "bcd_pass_kernel")[-n:]
     avg_us = sum(b - a for a, b in d) / len(d) / 1e3
     lines = _trace_table(tr, f"BCD solver, the Llama-3.1-8B set ({bench.SET_WORKLOAD})", tr_cmd)
-    lines += ["", f"Roofline launches (the last {n} plain pass launches of the run: T passes at a "
-                  f"time on layer 0's gate matrix, 14336x4096, alone on one stream): average "
+    lines += ["", f"Roofline launches (the last {n} plain pass launches of the run: the T passes "
+                  f"of solves of layer 0's gate matrix, 14336x4096, alone on one stream): average "
                   f"{avg_us:.2f} us in this trace; bench.py measured {res['roofline']['avg_launch_us']:.2f} us "
                   f"with events in the same run (its average includes one final column update per "
                   f"T passes).", "",
