@@ -229,8 +229,10 @@ template <> struct Grid<kGridInt4> {
   // Codes of N estimates; true if any of them may round differently at the
   // exact quotient (then the caller re-decides those with exact(); near()
   // tells which). diff is unused here.
+  static constexpr bool kTwoEnded = false;  // one rounding and its residual
+  static constexpr bool kSlotMask = false;
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     float flag = 0.0f;
 #pragma unroll
     for (int e = 0; e < N; ++e) q[e] = fast(y[e], flag);
@@ -299,9 +301,10 @@ template <> struct Grid<kGridE2M1> {
   // when both ends give the same codes those are the codes of x. Otherwise
   // returns true and the caller re-decides with exact(). A zero code may
   // come back as -0, which is arithmetically harmless.
-  // diff[g] receives the differing nibbles of group g (near() reads them).
+  // diff[g] receives the differing nibbles of group g (near() reads them),
+  // hiw[g] the codes at the upper ends (resolve() reads them).
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     static_assert(N % 8 == 0, "groups of 8");
     uint32_t any = 0u;
 #pragma unroll
@@ -315,6 +318,7 @@ template <> struct Grid<kGridE2M1> {
       }
       const uint32_t wl = cvt8(lo), wh = cvt8(hi);
       diff[g / 8] = wl ^ wh;
+      hiw[g / 8] = wh;
       any |= wl ^ wh;
       typedef float f2 __attribute__((ext_vector_type(2)));
       f2 r;
@@ -328,6 +332,40 @@ template <> struct Grid<kGridE2M1> {
   __device__ static __forceinline__ bool near(const float* y, const float* q, const uint32_t* diff,
                                               int e) {
     return ((diff[e >> 3] >> (4 * (e & 7))) & 0xFu) != 0u;
+  }
+  // Rounded by two conversions. Exact ties are the common case of differing
+  // ends here and stay rare enough per wave (an element in a few thousand
+  // on the workloads) that the re-decision visits only the slots some lane
+  // flags, found from the lanes' difference words (kSlotMask): field
+  // e % kPerWord of word e / kPerWord.
+  static constexpr bool kTwoEnded = true;
+  static constexpr bool kSlotMask = true;
+  static constexpr int kPerWord = 8;
+  __device__ static __forceinline__ uint32_t field(const uint32_t* d, int e) {
+    return (d[e >> 3] >> (4 * (e & 7))) & 0xFu;
+  }
+  // Exact code of element e from the codes at its bracket's ends: ql (the
+  // lower magnitude, decoded) and the upper one in hiw. Where they differ
+  // the exact quotient |x| is on one side of their midpoint m, or on it:
+  // the sign of |W| - m a b decides (m a b is exact: m has at most 3
+  // significant bits), a tie goes to the even encoding (the nibble's low
+  // bit is the mantissa bit). Where they agree the result is ql.
+  __device__ static __forceinline__ float resolve(float ql, const uint32_t* hiw, int e, float w, float a,
+                                                  float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const uint32_t wh = hiw[e >> 3];
+    f2 r;
+    switch ((e & 7) >> 1) {  // e is a compile-time constant at every call
+      case 0: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wh, 1.0f, 0); break;
+      case 1: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wh, 1.0f, 1); break;
+      case 2: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wh, 1.0f, 2); break;
+      default: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wh, 1.0f, 3); break;
+    }
+    const float qh = (e & 1) ? r.y : r.x;
+    const float m = 0.5f * (__builtin_fabsf(ql) + __builtin_fabsf(qh));
+    const float d = __builtin_fmaf(-(m * a), b, __builtin_fabsf(w));
+    const bool hi_even = ((wh >> (4 * (e & 7))) & 1u) == 0u;
+    return (d > 0.0f || (d == 0.0f && hi_even)) ? qh : ql;
   }
   // Codes of N quotients that are exact: the conversion's own rounding is
   // the decision (a zero may come back as -0).
@@ -383,8 +421,10 @@ template <> struct Grid<kGridInt8> {
     const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
     return __builtin_amdgcn_fmed3f(k + up, -127.0f, 127.0f);
   }
+  static constexpr bool kTwoEnded = false;
+  static constexpr bool kSlotMask = false;
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     float flag = 0.0f;
 #pragma unroll
     for (int e = 0; e < N; ++e) q[e] = fast(y[e], flag);
@@ -447,9 +487,9 @@ template <> struct Grid<kGridE4M3> {
   // Codes of N estimates by the same two-ended certificate as E2M1: the
   // exact quotient lies in [y (1 - 2^-20), y (1 + 2^-20)]; equal codes at
   // both ends are its codes. diff[g] receives the differing bytes of group
-  // g of 4 elements.
+  // g of 4 elements (hiw is not used).
   template <int N>
-  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff) {
+  __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     static_assert(N % 4 == 0, "groups of 4");
     uint32_t any = 0u;
 #pragma unroll
@@ -475,6 +515,11 @@ template <> struct Grid<kGridE4M3> {
                                               int e) {
     return ((diff[e >> 2] >> (8 * (e & 3))) & 0xFFu) != 0u;
   }
+  // Rounded by two conversions; with eight levels per binade its ties are
+  // more frequent than E2M1's and spread over more lanes, where testing each
+  // slot with a vector compare is the cheaper re-decision (no kSlotMask).
+  static constexpr bool kTwoEnded = true;
+  static constexpr bool kSlotMask = false;
   // Codes of N quotients that are exact: the conversion's own rounding is
   // the decision (magnitudes up to 456 saturate to 448).
   template <int N>

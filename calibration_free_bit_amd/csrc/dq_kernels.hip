@@ -44,6 +44,49 @@ __device__ __forceinline__ bool wave_any(bool p) {
   return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
+// Re-decide exactly the element slots of N fast codes where some lane of
+// the wave may differ from the exact rounding (after fast_n returned true
+// in some lane). w: the weights, a: the block scale of each group of BL
+// elements, b: the column scale of each element. Under kSlotMask the lanes
+// whose ends differ are few (about one per flagged wave on the workloads):
+// their difference words are OR-ed into scalar registers, so the slots are
+// tested by scalar branches and only those where some lane differs are
+// re-decided. Otherwise (or with MASK false) each slot is tested with a
+// vector compare.
+template <int GRID, int N, int BL, bool MASK = Grid<GRID>::kSlotMask>
+__device__ __forceinline__ void redecide(const float* y, float* q, const uint32_t* diff, const uint32_t* hiw,
+                                         const float* w, const float* a, const float* b) {
+  using Gr = Grid<GRID>;
+  if constexpr (MASK) {
+    constexpr int ND = N / Gr::kPerWord;
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) mine |= diff[d];
+    uint64_t lanes = __builtin_amdgcn_ballot_w64(mine != 0u);
+    uint32_t D[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) D[d] = 0u;
+    while (lanes != 0u) {
+      const int l = __builtin_ctzll(lanes);
+      lanes &= lanes - 1u;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) D[d] |= (uint32_t)__builtin_amdgcn_readlane((int)diff[d], l);
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (Gr::field(D, e) != 0u) {
+        // the new code replaces q[e] in its own register (a tied operand),
+        // so that the path without re-decisions needs no register copies
+        const float r = Gr::resolve(q[e], hiw, e, w[e], a[e / BL], b[e]);
+        asm("v_mov_b32 %0, %1" : "+v"(q[e]) : "v"(r));
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (wave_any(Gr::near(y, q, diff, e))) q[e] = Gr::exact(y[e], w[e], a[e / BL], b[e]);
+  }
+}
+
 // The value of lane (lane ^ M) within each quad of lanes (M = 1 or 2), by a
 // DPP quad permutation (VALU moves instead of an LDS round trip). Every
 // source lane of a quad permutation exists, so bound_ctrl (zero for a
@@ -422,8 +465,23 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
     }
     __syncthreads();
 
+    // this lane's column scales and their reciprocals. For the grids rounded
+    // by two conversions they are copied to registers for the whole segment:
+    // read through the LDS pointers, the compiler kept two copies of the
+    // codes across the re-decision branch (16 register moves per row step);
+    // the integer grids compile to the same loop either way and read LDS.
+    float lb_r[LC], lrb_r[LC];
     const float* lb = s_b + sub * LC;
     const float* lrb = s_rb + sub * LC;
+    if constexpr (Grid<GRID>::kTwoEnded) {
+#pragma unroll
+      for (int e = 0; e < LC; ++e) {
+        lb_r[e] = s_b[sub * LC + e];
+        lrb_r[e] = s_rb[sub * LC + e];
+      }
+      lb = lb_r;
+      lrb = lrb_r;
+    }
     double cn[LC], cd[LC];
 #pragma unroll
     for (int e = 0; e < LC; ++e) { cn[e] = 0.0; cd[e] = 0.0; }
@@ -559,18 +617,9 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         if constexpr (kExactQ) {
           Grid<GRID>::template nearest_n<LC>(y, q);
         } else {
-          uint32_t diff[LC / 4];
-          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
-            // only the element slots where some lane is near a midpoint
-#pragma unroll
-            for (int bl = 0; bl < NB; ++bl)
-#pragma unroll
-              for (int k = 0; k < BL; ++k) {
-                const int e = bl * BL + k;
-                if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                  q[e] = Grid<GRID>::exact(y[e], w[e], a_old[bl], lb[e]);
-              }
-          }
+          uint32_t diff[LC / 4], hiw[LC / 4];
+          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_old, lb);
         }
         row_sums_f32();
       }
@@ -649,17 +698,9 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         if constexpr (kExactQ) {
           Grid<GRID>::template nearest_n<LC>(y, q);
         } else {
-          uint32_t diff[LC / 4];
-          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff))) {
-#pragma unroll
-            for (int bl = 0; bl < NB; ++bl)
-#pragma unroll
-              for (int k = 0; k < BL; ++k) {
-                const int e = bl * BL + k;
-                if (wave_any(Grid<GRID>::near(y, q, diff, e)))
-                  q[e] = Grid<GRID>::exact(y[e], w[e], a_new[bl], lb[e]);
-              }
-          }
+          uint32_t diff[LC / 4], hiw[LC / 4];
+          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_new, lb);
         }
       }
 
@@ -796,15 +837,9 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
 #pragma unroll
       for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
     }
-    uint32_t diff[4];
-    if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff))) {
-#pragma unroll
-      for (int bl = 0; bl < NB; ++bl)
-#pragma unroll
-        for (int k = bl * BL; k < (bl + 1) * BL; ++k)
-          if (wave_any(Grid<GRID>::near(y, q, diff, k)))
-            q[k] = Grid<GRID>::exact(y[k], w[k], av[bl], bj[k]);
-    }
+    uint32_t diff[4], hiw[4];
+    if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff, hiw)))
+      redecide<GRID, 16, BL>(y, q, diff, hiw, w, av, bj);
     const Word c0 = Grid<GRID>::encode8(q), c1 = Grid<GRID>::encode8(q + 8);
     if (ok && (!REPORT || packed)) {
       uint8_t* dst = packed + row * (N * B / 8) + col * B / 8;
@@ -936,12 +971,10 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
       const float rs = __builtin_amdgcn_rcpf(sf);
 #pragma unroll
       for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
-      uint32_t diff[2];
-      if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff))) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (wave_any(Grid<GRID>::near(y, q, diff, k))) q[k] = Grid<GRID>::exact(y[k], x[k], sf, 1.0f);
-      }
+      uint32_t diff[2], hiw[2];
+      const float one[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+      if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff, hiw)))
+        redecide<GRID, 8, 8, false>(y, q, diff, hiw, x, &sf, one);  // per slot: measured faster here
     }
     if (live && t < T) {
       Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
