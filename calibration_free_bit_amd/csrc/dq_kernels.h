@@ -8,8 +8,7 @@
 namespace dq {
 
 constexpr int kTileCols = 64;   // columns of one independent tile
-constexpr int kLaneCols = 16;   // contiguous columns one lane owns
-constexpr int kRowsPerStep = 4 * 64 * kLaneCols / kTileCols;  // rows per workgroup step
+constexpr int kRowsPerStep = 64;  // rows of one BCD pass workgroup step
 constexpr int kPassGrid = 512;  // target workgroups of one BCD pass (two per CU)
 
 // Geometry of one BCD pass. Work is the flattened list of (tile, row step)

@@ -11,8 +11,8 @@
 // The row/block update only needs the G columns of its block and the column
 // update only needs a' of the same column stripe, so the problem splits into
 // independent 64-column tiles spanning all rows. A workgroup streams a range
-// of row steps of a tile: every lane owns kLaneCols contiguous columns of one
-// row, keeps those elements in registers between the two requantizations,
+// of row steps of a tile: every lane owns LC (16 or 8) contiguous columns of
+// one row, keeps those elements in registers between the two requantizations,
 // and accumulates float64 column sums for its columns across the rows it
 // visits. At the end of its range the workgroup reduces those sums through
 // LDS and writes one partial per column. The column update b' is formed by
@@ -116,6 +116,17 @@ __device__ __forceinline__ double half_mirror(double v) {
   const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), 0x141, 0xF, 0xF, false);
   const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), 0x141, 0xF, 0xF, false);
   return __hiloint2double(hi, lo);
+}
+// Sum of v over the aligned group of K lanes (K = 1, 2, 4 or 8) holding
+// this lane, in every lane of the group: pairs, then quads, then the two
+// quads of a group of 8. The order of the additions is fixed.
+template <int K, class T>
+__device__ __forceinline__ T lane_join(T v) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8, "groups of 1, 2, 4 or 8 lanes");
+  if constexpr (K >= 2) v += quad_xor<1>(v);
+  if constexpr (K >= 4) v += quad_xor<2>(v);
+  if constexpr (K >= 8) v += half_mirror(v);
+  return v;
 }
 
 // ------------------------------------------------------------------ init
@@ -292,7 +303,26 @@ __global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kRowSure = 0x1p-19f;  // bracket of the float32 row sums (32 units of 2^-24)
 constexpr int kPrefetch = 1;   // row steps in flight per lane
-constexpr int kPassOcc = 2;    // workgroups per CU the register budget must allow
+
+// Columns per lane of a pass. A workgroup step always covers 64 rows of a
+// 64-column tile, with 4 waves of 16 columns per lane or 8 waves of 8; two
+// workgroups share a CU either way, so the narrower lanes give each SIMD 4
+// waves instead of 2 for about 10 % more instructions per element (the
+// per-row work is shared by fewer elements) within 128 registers per lane.
+// Measured per pass: the 8-column form is faster where the second
+// requantization is mostly skipped and memory waits are longer (power-of-
+// two and E4M3 block scales: NVFP4 4096x14336 54.0 -> 48.6 us, MXINT4
+// 14336x4096 38.6 -> 36.2 us), the 16-column form where it runs for almost
+// every wave (fp16 block scales, which move every iteration: INT4-G64
+// 14336x4096 38.3 against 39.9 us).
+template <int AFMT>
+constexpr int pass_lane_cols() {
+  return AFMT == kScaleFp16 ? 16 : 8;
+}
+template <int LC>
+constexpr int pass_threads() {
+  return 64 * (kRowsPerStep * kTileCols / (64 * LC));
+}
 
 // Column update from the partials of one pass: b'_j = Pi_fp16(sum num /
 // sum den) over the segments of column j's tile, added in segment order.
@@ -373,8 +403,8 @@ struct PassStats {
 // b in memory.
 enum : int { kPassPlain = 0, kPassStats = 1, kPassInit = 2 };
 
-template <int WT, int GRID, int AFMT, int G, int MODE>
-__global__ void __launch_bounds__(kThreads, kPassOcc)
+template <int WT, int GRID, int AFMT, int G, int MODE, int LC>
+__global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
     bcd_pass_kernel(const void* __restrict__ W, const double* __restrict__ part_in, void* __restrict__ a_,
                     int32_t gM, int32_t gN, int32_t gldw, int32_t gS, int32_t gL, int32_t gtotal,
                     int32_t gn_tiles, int32_t gmax_seg, const uint16_t* __restrict__ b,
@@ -393,10 +423,10 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
   // decision itself (no tie flag, no exact re-decision).
   constexpr bool kExactQ = INIT && AFMT == kScaleE8M0;
   constexpr int CB = Grid<GRID>::kBits;     // bits per stored code
-  constexpr int LC = kLaneCols;             // contiguous columns per lane
+  constexpr int PT = pass_threads<LC>();     // threads (two workgroups per CU: PT / 128 waves per SIMD)
   constexpr int LPR = kTileCols / LC;       // lanes per row of a tile
   constexpr int RPW = 64 / LPR;             // rows per wave per step
-  constexpr int RPS = 4 * RPW;              // rows per workgroup per step
+  constexpr int RPS = PT / 64 * RPW;        // rows per workgroup per step
   constexpr int BL = G < LC ? G : LC;       // elements of one block inside a lane
   constexpr int NB = LC / BL;               // blocks (or block parts) per lane
   constexpr int LPB = G > LC ? G / LC : 1;  // lanes sharing one block
@@ -407,11 +437,12 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
   constexpr int kRedStride = 68;
   constexpr int EB = WT == kWBF16 ? 2 : 4;  // bytes per W element
   static_assert(RPS == kRowsPerStep, "geometry mismatch");
-  static_assert(LC == 16, "a lane's columns are all in range or all out (N % 16 == 0)");
+  static_assert(LC == 8 || LC == 16, "a lane's columns are all in range or all out (N % 16 == 0)");
+  static_assert(LPR <= 8 && LPB <= LPR, "a block's lanes lie in one group of 8 (lane_join)");
   static_assert(RPS == 64, "the reduction's LDS pitch assumes 64 row-lanes");
 
-  __shared__ float s_b[kTileCols];
-  __shared__ float s_rb[kTileCols];
+  __shared__ __align__(16) float s_b[kTileCols];
+  __shared__ __align__(16) float s_rb[kTileCols];
   __shared__ double s_red[kTileCols * kRedStride];
 
   const int tid = threadIdx.x;
@@ -465,15 +496,18 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
     }
     __syncthreads();
 
-    // this lane's column scales and their reciprocals. For the grids rounded
-    // by two conversions they are copied to registers for the whole segment:
-    // read through the LDS pointers, the compiler kept two copies of the
-    // codes across the re-decision branch (16 register moves per row step);
-    // the integer grids compile to the same loop either way and read LDS.
+    // this lane's column scales and their reciprocals. With 16 columns per
+    // lane and the grids rounded by two conversions they are copied to
+    // registers for the whole segment: read through the LDS pointers, the
+    // compiler kept two copies of the codes across the re-decision branch
+    // (16 register moves per row step); the integer grids compile to the
+    // same loop either way and read LDS. With 8 columns per lane each row
+    // step reads them from LDS (below), which keeps the 128-register budget.
     float lb_r[LC], lrb_r[LC];
     const float* lb = s_b + sub * LC;
     const float* lrb = s_rb + sub * LC;
-    if constexpr (Grid<GRID>::kTwoEnded) {
+    int lds_off4 = sub * LC / 4;  // the lane's first column scale, in float4 units
+    if constexpr (LC == 16 && Grid<GRID>::kTwoEnded) {
 #pragma unroll
       for (int e = 0; e < LC; ++e) {
         lb_r[e] = s_b[sub * LC + e];
@@ -498,6 +532,23 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
     // in-flight register is ever copied (the loop below is unrolled by
     // kPrefetch).
     auto row_step = [&]<int SLOT>() {
+      const float* lbs = lb;
+      const float* lrbs = lrb;
+      float lb8[LC], lrb8[LC];
+      if constexpr (LC == 8) {
+        // an opaque offset keeps these loads inside the loop
+        asm volatile("" : "+v"(lds_off4));
+        const float4* b4 = reinterpret_cast<const float4*>(s_b) + lds_off4;
+        const float4* rb4 = reinterpret_cast<const float4*>(s_rb) + lds_off4;
+#pragma unroll
+        for (int i = 0; i < LC / 4; ++i) {
+          const float4 u = b4[i], v = rb4[i];
+          lb8[4 * i] = u.x; lb8[4 * i + 1] = u.y; lb8[4 * i + 2] = u.z; lb8[4 * i + 3] = u.w;
+          lrb8[4 * i] = v.x; lrb8[4 * i + 1] = v.y; lrb8[4 * i + 2] = v.z; lrb8[4 * i + 3] = v.w;
+        }
+        lbs = lb8;
+        lrbs = lrb8;
+      }
       const bool row_ok = row < M32;
       // rows past M occur only in the last step of a tile, columns past N
       // only in the last tile
@@ -518,6 +569,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         }
         if constexpr (LPB >= 2) amax[0] = __builtin_fmaxf(amax[0], quad_xor<1>(amax[0]));
         if constexpr (LPB >= 4) amax[0] = __builtin_fmaxf(amax[0], quad_xor<2>(amax[0]));
+        if constexpr (LPB >= 8) amax[0] = __builtin_fmaxf(amax[0], half_mirror(amax[0]));
         bool unsure = false;
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
@@ -563,9 +615,10 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
       // per lane. Every term W R and R^2 is non-negative (a non-zero code
       // has the sign of its weight), so each fused multiply-add adds at most
       // one rounding of a partial sum no larger than the whole sum: at most
-      // 8 units of 2^-24 (relative) per chain, one for joining the chains
-      // and one per join across the lanes of a block (two for G = 64), 11
-      // for the numerator and the denominator alike. Their quotient with a
+      // BL / 2 units of 2^-24 (relative) per chain, one for joining the
+      // chains and one per join across the lanes of a block (log2 LPB), at
+      // most 11 (BL = 16, G = 64) for the numerator and the denominator
+      // alike. Their quotient with a
       // 1-ulp reciprocal is then within 25 units, inside the certified
       // projection's bracket of kRowSure = 32 units. A wave with a block
       // the bracket cannot decide redoes its sums in float64, where every
@@ -578,7 +631,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
 #pragma unroll
           for (int k = 0; k < BL; k += 2) {
             const int e = bl * BL + k;
-            const float R0 = q[e] * lb[e], R1 = q[e + 1] * lb[e + 1];  // exact products
+            const float R0 = q[e] * lbs[e], R1 = q[e + 1] * lbs[e + 1];  // exact products
             n0 = __builtin_fmaf(w[e], R0, n0);
             d0 = __builtin_fmaf(R0, R0, d0);
             n1 = __builtin_fmaf(w[e + 1], R1, n1);
@@ -597,7 +650,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
 #pragma unroll
           for (int k = 0; k < BL; ++k) {
             const int e = bl * BL + k;
-            const double R = (double)(q[e] * lb[e]);  // exact product
+            const double R = (double)(q[e] * lbs[e]);  // exact product
             num[bl] = __builtin_fma((double)w[e], R, num[bl]);
             den[bl] = __builtin_fma(R, R, den[bl]);
           }
@@ -609,7 +662,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         for (int bl = 0; bl < NB; ++bl)
           ra[bl] = recip_scale<AFMT>(a_old[bl]);
 #pragma unroll
-        for (int e = 0; e < LC; ++e) wrb[e] = w[e] * lrb[e];
+        for (int e = 0; e < LC; ++e) wrb[e] = w[e] * lrbs[e];
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
@@ -619,7 +672,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         } else {
           uint32_t diff[LC / 4], hiw[LC / 4];
           if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
-            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_old, lb);
+            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_old, lbs);
         }
         row_sums_f32();
       }
@@ -633,29 +686,22 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
               const int e = bl * BL + k;
               // a Q b is exact in float64: q b is exact in float32
               const double wk = (double)w[e];
-              const double d = wk - (double)(q[e] * lb[e]) * (double)a_old[bl];
+              const double d = wk - (double)(q[e] * lbs[e]) * (double)a_old[bl];
               st_sse = __builtin_fma(d, d, st_sse);
               st_w2 = __builtin_fma(wk, wk, st_w2);
             }
           uint8_t* cp = st.codes + row * (g.N * CB / 8) + ccol * CB / 8;
-          const Word c0 = Grid<GRID>::encode8(q), c1 = Grid<GRID>::encode8(q + 8);
-          if (st.has_prev)
-            st_changed += Grid<GRID>::count_diff(c0, *reinterpret_cast<const Word*>(cp)) +
-                          Grid<GRID>::count_diff(c1, *reinterpret_cast<const Word*>(cp + CB));
-          *reinterpret_cast<Word*>(cp) = c0;
-          *reinterpret_cast<Word*>(cp + CB) = c1;
+#pragma unroll
+          for (int i = 0; i < LC / 8; ++i) {  // 8 codes per word, CB bytes
+            const Word c = Grid<GRID>::encode8(q + 8 * i);
+            if (st.has_prev) st_changed += Grid<GRID>::count_diff(c, *reinterpret_cast<const Word*>(cp + i * CB));
+            *reinterpret_cast<Word*>(cp + i * CB) = c;
+          }
         }
       }
-      // blocks wider than a lane: the lanes of a block form (part of) a quad
-      static_assert(LPB <= 4 && LPR == 4, "a block's lanes lie in one quad");
-      if constexpr (LPB >= 2) {
-        numf[0] += quad_xor<1>(numf[0]);
-        denf[0] += quad_xor<1>(denf[0]);
-      }
-      if constexpr (LPB >= 4) {
-        numf[0] += quad_xor<2>(numf[0]);
-        denf[0] += quad_xor<2>(denf[0]);
-      }
+      // blocks wider than a lane: add the sums of the block's lanes
+      numf[0] = lane_join<LPB>(numf[0]);
+      denf[0] = lane_join<LPB>(denf[0]);
 
       // project, synchronize the copy that assigns codes, store. The
       // float32 denominator is 0 exactly when every code of the block is 0
@@ -667,14 +713,8 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         a_new[bl] = denf[bl] > 0.0f ? project_certified<AFMT>(numf[bl], denf[bl], kRowSure, unsure) : 1.0f;
       if (wave_any(unsure)) {
         row_sums_f64();
-        if constexpr (LPB >= 2) {
-          num[0] += quad_xor<1>(num[0]);
-          den[0] += quad_xor<1>(den[0]);
-        }
-        if constexpr (LPB >= 4) {
-          num[0] += quad_xor<2>(num[0]);
-          den[0] += quad_xor<2>(den[0]);
-        }
+        num[0] = lane_join<LPB>(num[0]);
+        den[0] = lane_join<LPB>(den[0]);
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl) a_new[bl] = (float)ls_scale<AFMT>(num[bl], den[bl]);
       }
@@ -700,7 +740,7 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         } else {
           uint32_t diff[LC / 4], hiw[LC / 4];
           if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
-            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_new, lb);
+            redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_new, lbs);
         }
       }
 
@@ -740,13 +780,13 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
         s_red[(e * LPR + sub) * kRedStride + wave * RPW + rl] = qn ? cd[e] : cn[e];
       }
       __syncthreads();
-      const int cr = tid >> 2, pi = tid & 3;  // LDS row, quarter of the row-lanes
+      constexpr int kParts = PT / kTileCols;  // threads per LDS row
+      const int cr = tid / kParts, pi = tid % kParts;    // LDS row, part of its row-lanes
       double acc = 0.0;
       const int c = (cr % LPR) * LC + cr / LPR;  // the column of LDS row cr
 #pragma unroll 8
-      for (int r = 0; r < RPS / 4; ++r) acc += s_red[cr * kRedStride + r * 4 + pi];
-      acc += quad_xor<1>(acc);
-      acc += quad_xor<2>(acc);
+      for (int r = 0; r < RPS / kParts; ++r) acc += s_red[cr * kRedStride + r * kParts + pi];
+      acc = lane_join<kParts>(acc);
       if (pi == 0) pw[c * 2 + qn] = acc;
       __syncthreads();
     }
@@ -754,15 +794,15 @@ __global__ void __launch_bounds__(kThreads, kPassOcc)
 
   if constexpr (STATS) {  // s_red is free: every segment ended with a barrier
     s_red[tid] = st_sse;
-    s_red[kThreads + tid] = st_w2;
-    s_red[2 * kThreads + tid] = (double)st_changed;
+    s_red[PT + tid] = st_w2;
+    s_red[2 * PT + tid] = (double)st_changed;
     __syncthreads();
-    for (int h = kThreads / 2; h > 0; h >>= 1) {
+    for (int h = PT / 2; h > 0; h >>= 1) {
       if (tid < h)
-        for (int i = 0; i < 3; ++i) s_red[i * kThreads + tid] += s_red[i * kThreads + tid + h];
+        for (int i = 0; i < 3; ++i) s_red[i * PT + tid] += s_red[i * PT + tid + h];
       __syncthreads();
     }
-    if (tid < 3) st.part[(int64_t)blockIdx.x * 3 + tid] = s_red[tid * kThreads];
+    if (tid < 3) st.part[(int64_t)blockIdx.x * 3 + tid] = s_red[tid * PT];
   }
 }
 
@@ -1019,7 +1059,8 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
 template <int WT, int GRID, int AFMT, int G, int MODE>
 hipError_t launch_pass(const void* W, const double* in, void* a, uint16_t* b, double* out,
                        const PassGeom& g, const PassStats& ps, hipStream_t st) {
-  bcd_pass_kernel<WT, GRID, AFMT, G, MODE><<<(unsigned)g.n_wg, kThreads, 0, st>>>(
+  constexpr int LC = pass_lane_cols<AFMT>();
+  bcd_pass_kernel<WT, GRID, AFMT, G, MODE, LC><<<(unsigned)g.n_wg, pass_threads<LC>(), 0, st>>>(
       W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
       (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps);
   return hipGetLastError();
