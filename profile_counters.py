@@ -83,12 +83,13 @@ def _find(root, suffix):
 
 def _matches(kernel_name: str, name_has: str) -> bool:
     """name_has in the kernel's name; for the pass kernel only its plain
-    instantiation (last template argument 0), not the first pass of a
-    whole solve or the statistics variant."""
+    instantiation (fifth template argument, the pass mode, 0), not the first
+    pass of a whole solve or the statistics variant."""
     if name_has not in kernel_name:
         return False
     if name_has == "bcd_pass_kernel":
-        return kernel_name.split(">(")[0].endswith(", 0")
+        args = kernel_name.split("<", 1)[1].split(">(")[0].split(",")
+        return args[4].strip() == "0"
     return True
 
 
