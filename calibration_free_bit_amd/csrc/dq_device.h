@@ -231,6 +231,7 @@ template <> struct Grid<kGridInt4> {
   // tells which). diff is unused here.
   static constexpr bool kTwoEnded = false;  // one rounding and its residual
   static constexpr bool kSlotMask = false;
+  static constexpr bool kScaledEnds = false;
   template <int N>
   __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     float flag = 0.0f;
@@ -333,6 +334,40 @@ template <> struct Grid<kGridE2M1> {
                                               int e) {
     return ((diff[e >> 3] >> (4 * (e & 7))) & 0xFu) != 0u;
   }
+  // fast_n of the quotients wrb[e] * ra[e / BL] (wrb = W / b, ra = 1 / a,
+  // both from 1-ulp reciprocals) without forming them: the two ends come
+  // from the block's reciprocal scaled by 1 -+ 2^-20, each within 7 units
+  // of 2^-24 of x (1 -+ 2^-20) (two reciprocals, three roundings), so x
+  // lies between them. No clamp: the conversion saturates at +-6 for every
+  // larger magnitude, infinities included.
+  static constexpr bool kScaledEnds = true;
+  template <int N, int BL>
+  __device__ static __forceinline__ bool fast_scaled(const float* wrb, const float* ra, float* q, uint32_t* diff,
+                                                     uint32_t* hiw) {
+    static_assert(N % 8 == 0 && (BL % 8 == 0 || 8 % BL == 0), "groups of 8");
+    uint32_t any = 0u;
+#pragma unroll
+    for (int g = 0; g < N; g += 8) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float r = ra[(g + k) / BL];
+        lo[k] = wrb[g + k] * (r * (1.0f - 0x1p-20f));
+        hi[k] = wrb[g + k] * (r * (1.0f + 0x1p-20f));
+      }
+      const uint32_t wl = cvt8(lo), wh = cvt8(hi);
+      diff[g / 8] = wl ^ wh;
+      hiw[g / 8] = wh;
+      any |= wl ^ wh;
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 r;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 0); q[g + 0] = r.x; q[g + 1] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 1); q[g + 2] = r.x; q[g + 3] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 2); q[g + 4] = r.x; q[g + 5] = r.y;
+      r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wl, 1.0f, 3); q[g + 6] = r.x; q[g + 7] = r.y;
+    }
+    return any != 0u;
+  }
   // Rounded by two conversions. Exact ties are the common case of differing
   // ends here and stay rare enough per wave (an element in a few thousand
   // on the workloads) that the re-decision visits only the slots some lane
@@ -423,6 +458,7 @@ template <> struct Grid<kGridInt8> {
   }
   static constexpr bool kTwoEnded = false;
   static constexpr bool kSlotMask = false;
+  static constexpr bool kScaledEnds = false;
   template <int N>
   __device__ static __forceinline__ bool fast_n(const float* y, float* q, uint32_t* diff, uint32_t* hiw) {
     float flag = 0.0f;
@@ -520,6 +556,7 @@ template <> struct Grid<kGridE4M3> {
   // slot with a vector compare is the cheaper re-decision (no kSlotMask).
   static constexpr bool kTwoEnded = true;
   static constexpr bool kSlotMask = false;
+  static constexpr bool kScaledEnds = false;
   // Codes of N quotients that are exact: the conversion's own rounding is
   // the decision (magnitudes up to 456 saturate to 448).
   template <int N>

@@ -663,16 +663,22 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
           ra[bl] = recip_scale<AFMT>(a_old[bl]);
 #pragma unroll
         for (int e = 0; e < LC; ++e) wrb[e] = w[e] * lrbs[e];
-#pragma unroll
-        for (int bl = 0; bl < NB; ++bl)
-#pragma unroll
-          for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
-        if constexpr (kExactQ) {
-          Grid<GRID>::template nearest_n<LC>(y, q);
-        } else {
+        if constexpr (Grid<GRID>::kScaledEnds && !kExactQ) {
           uint32_t diff[LC / 4], hiw[LC / 4];
-          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+          if (wave_any(Grid<GRID>::template fast_scaled<LC, BL>(wrb, ra, q, diff, hiw)))
             redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_old, lbs);
+        } else {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+            for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
+          if constexpr (kExactQ) {
+            Grid<GRID>::template nearest_n<LC>(y, q);
+          } else {
+            uint32_t diff[LC / 4], hiw[LC / 4];
+            if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+              redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_old, lbs);
+          }
         }
         row_sums_f32();
       }
@@ -728,19 +734,25 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
 #pragma unroll
       for (int bl = 0; bl < NB; ++bl) changed |= a_new[bl] != a_old[bl];
       if (wave_any(changed)) {
-        float y[LC];
+        float ra[NB], y[LC];
 #pragma unroll
-        for (int bl = 0; bl < NB; ++bl) {
-          const float ra = recip_scale<AFMT>(a_new[bl]);
-#pragma unroll
-          for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra;
-        }
-        if constexpr (kExactQ) {
-          Grid<GRID>::template nearest_n<LC>(y, q);
-        } else {
+        for (int bl = 0; bl < NB; ++bl) ra[bl] = recip_scale<AFMT>(a_new[bl]);
+        if constexpr (Grid<GRID>::kScaledEnds && !kExactQ) {
           uint32_t diff[LC / 4], hiw[LC / 4];
-          if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+          if (wave_any(Grid<GRID>::template fast_scaled<LC, BL>(wrb, ra, q, diff, hiw)))
             redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_new, lbs);
+        } else {
+#pragma unroll
+          for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+            for (int k = 0; k < BL; ++k) y[bl * BL + k] = wrb[bl * BL + k] * ra[bl];
+          if constexpr (kExactQ) {
+            Grid<GRID>::template nearest_n<LC>(y, q);
+          } else {
+            uint32_t diff[LC / 4], hiw[LC / 4];
+            if (wave_any(Grid<GRID>::template fast_n<LC>(y, q, diff, hiw)))
+              redecide<GRID, LC, BL>(y, q, diff, hiw, w, a_new, lbs);
+          }
         }
       }
 
