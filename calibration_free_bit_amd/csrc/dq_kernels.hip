@@ -883,15 +883,25 @@ __global__ void __launch_bounds__(256) pack_kernel(const void* __restrict__ W, i
       av[bl] = decode_scale<AFMT>(reinterpret_cast<const AT*>(a_)[row * (N / G) + (col + bl * BL) / G]);
     float w[16], y[16], q[16];
     raw.unpack(w);
-#pragma unroll
-    for (int bl = 0; bl < NB; ++bl) {
-      const float ra = recip_scale<AFMT>(av[bl]);
-#pragma unroll
-      for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
-    }
     uint32_t diff[4], hiw[4];
-    if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff, hiw)))
-      redecide<GRID, 16, BL>(y, q, diff, hiw, w, av, bj);
+    if constexpr (Grid<GRID>::kScaledEnds) {
+      float wrb[16], ra[NB];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) wrb[k] = w[k] * rb[k];
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) ra[bl] = recip_scale<AFMT>(av[bl]);
+      if (wave_any(Grid<GRID>::template fast_scaled<16, BL>(wrb, ra, q, diff, hiw)))
+        redecide<GRID, 16, BL>(y, q, diff, hiw, w, av, bj);
+    } else {
+#pragma unroll
+      for (int bl = 0; bl < NB; ++bl) {
+        const float ra = recip_scale<AFMT>(av[bl]);
+#pragma unroll
+        for (int k = bl * BL; k < (bl + 1) * BL; ++k) y[k] = w[k] * rb[k] * ra;
+      }
+      if (wave_any(Grid<GRID>::template fast_n<16>(y, q, diff, hiw)))
+        redecide<GRID, 16, BL>(y, q, diff, hiw, w, av, bj);
+    }
     const Word c0 = Grid<GRID>::encode8(q), c1 = Grid<GRID>::encode8(q + 8);
     if (ok && (!REPORT || packed)) {
       uint8_t* dst = packed + row * (N * B / 8) + col * B / 8;
@@ -1021,12 +1031,17 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
       Grid<GRID>::template nearest_n<8>(y, q);
     } else {
       const float rs = __builtin_amdgcn_rcpf(sf);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
       uint32_t diff[2], hiw[2];
       const float one[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
-      if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff, hiw)))
-        redecide<GRID, 8, 8, false>(y, q, diff, hiw, x, &sf, one);  // per slot: measured faster here
+      if constexpr (Grid<GRID>::kScaledEnds) {
+        if (wave_any(Grid<GRID>::template fast_scaled<8, 8>(x, &rs, q, diff, hiw)))
+          redecide<GRID, 8, 8>(y, q, diff, hiw, x, &sf, one);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = x[k] * rs;
+        if (wave_any(Grid<GRID>::template fast_n<8>(y, q, diff, hiw)))
+          redecide<GRID, 8, 8, false>(y, q, diff, hiw, x, &sf, one);  // per slot: measured faster here
+      }
     }
     if (live && t < T) {
       Grid<GRID>::store8(xq + t * (N * B / 8) + col * B / 8, q);
