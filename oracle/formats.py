@@ -78,7 +78,10 @@ def round_e2m1(x: np.ndarray) -> np.ndarray:
     Returns float64 grid values.
     """
     x = np.asarray(x, dtype=np.float64)
-    ax = np.abs(x)
+    # every magnitude from 6 up has 6 as its nearest level; taking it there
+    # first keeps the distances exact (far above 6, |x| - level would round
+    # to the same float64 for every level)
+    ax = np.minimum(np.abs(x), E2M1_LEVELS[-1])
     dist = np.abs(ax[..., None] - E2M1_LEVELS)          # [..., 8]
     best = dist.min(axis=-1, keepdims=True)
     cand = dist == best                                   # one or two True

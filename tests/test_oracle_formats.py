@@ -75,6 +75,22 @@ def test_e2m1_rounding_matches_brute_force_incl_every_midpoint():
     assert not np.signbit(F.round_e2m1(np.array([-0.1])))[0]
 
 
+def test_huge_magnitudes_saturate_on_every_grid():
+    """Above the largest level the nearest level is the largest one, for any
+    magnitude ([DQ summary] §3 formats; reading: saturation). Far above it
+    float64 cannot tell the levels' distances apart, so the rounding must
+    not rely on them there."""
+    big = np.array([500.0 * 2.0 ** k for k in (0, 20, 60, 200, 1000)] + [np.inf])
+    x = np.concatenate([big, -big])
+    top = {"e2m1": 6.0, "e4m3": 448.0}
+    for grid in ("e2m1", "e4m3"):
+        want = np.where(x < 0, -top[grid], top[grid])
+        np.testing.assert_array_equal(F.round_to_grid(x, grid), want)
+    for grid in ("int4", "int8"):
+        lo, hi = F.INT_GRIDS[grid]
+        np.testing.assert_array_equal(F.round_to_grid(x, grid), np.where(x < 0, lo, hi))
+
+
 def test_tie_mask_flags_exact_midpoints_only():
     x = np.array([0.5, 0.5000001, 2.5, -7.5, 7.5, -8.5, 3.0])
     assert list(F.tie_mask(x, "int4")) == [True, False, True, True, False, False, False]
