@@ -16,7 +16,8 @@ import torch
 
 from calibration_free_bit_amd import dq, synth
 from oracle import dualquant as D
-from tests.gpu_util import ALL_FORMATS, DeviceRun, as_f64, compare, oracle_fmt
+from oracle import formats as F
+from tests.gpu_util import AFMT_NAME, ALL_FORMATS, DeviceRun, as_f64, compare, oracle_fmt
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +156,37 @@ def test_projection_range_ends(case, iters):
     h = DeviceRun(data, fmt).solve(iters)
     assert np.array_equal(h.a, g.a) and np.array_equal(h.b, g.b)
     np.testing.assert_array_equal(h.packed, g.packed)
+
+
+@pytest.mark.parametrize("iters", [1, 2])
+@pytest.mark.parametrize("name", ["nvfp4_g16", "mxfp4_g32"])
+def test_e2m1_codes_saturate_for_huge_quotients(name, iters):
+    """Resumed from the smallest legal block and column scales, W / (a b)
+    lies far above 6 for every weight, and past float32's range for the
+    large ones (a float32 estimate becomes infinite): the codes saturate at
+    +-6 on both sides. The E2M1 requantization forms its two bracket ends
+    without a clamp, relying on the conversion's saturation."""
+    fmt = NAMED[name]
+    ofmt = oracle_fmt(fmt)
+    rng = np.random.default_rng(11)
+    W = rng.normal(0, 0.02, (256, 256))
+    W[::17, ::13] = rng.choice([-1.0, 1.0], W[::17, ::13].shape) * 1e30
+    data = synth.bf16_bits(W)
+    W64 = as_f64(data)
+    M, N = W.shape
+    a0 = np.full((M, N // fmt.group), 2.0 ** -9 if fmt.a_fmt == dq.SCALE_E4M3 else 2.0 ** -127)
+    b0 = np.full(N, 2.0 ** -24)
+    sol = D.solve(W64, ofmt, iters, a=a0, b=b0)
+    print(f"[case] huge E2M1 quotients {name} T={iters}", flush=True)
+    g = DeviceRun(data, fmt)
+    a_bits = F.encode_scale(a0, AFMT_NAME[fmt.a_fmt])
+    g.s.a.copy_(torch.from_numpy(a_bits.view(np.int8 if a_bits.itemsize == 1 else np.int16)).cuda()
+                .view(g.s.a.dtype))
+    g.s.b.copy_(torch.from_numpy(F.encode_scale(b0, "fp16").view(np.int16)).cuda())
+    g.run(iters, init=False)
+    r = compare(W64, g.a, g.b, g.Q, sol, ofmt, f"huge quotients {name} T={iters}")
+    assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, r
+    np.testing.assert_array_equal(g.packed, D.pack_codes(sol.Q, ofmt))
 
 
 @pytest.mark.parametrize("name", ["mxint4_g32", "mxint8_g32", "mxfp8_g32"])
