@@ -51,6 +51,8 @@ struct Workspace {
   size_t pass_bytes;   // the two partial-sum buffers of the passes
   size_t codes_bytes;  // one state's codes (statistics)
   size_t stats_bytes;  // dq_bcd_iterate with statistics
+  size_t a_work_bytes; // the passes' tile-major block scales, after the partials (or 0)
+  bool a_tiled;        // the passes keep the block scales tile-major
 };
 
 Workspace pass_geometry(const dq_problem* p) {
@@ -81,14 +83,29 @@ Workspace pass_geometry(const dq_problem* p) {
   // the report uses [workgroups][3] float64
   const int64_t report_wg = dq::report_workgroups(p->rows, p->cols);
   const size_t report_bytes = size_t(report_wg) * 3 * sizeof(double);
-  w.bytes = align256(std::max({pass_bytes, init_bytes, report_bytes}));
-  // with statistics: the partials, then the codes of a state, then the
-  // per-workgroup sums of a pass or of the final report
+  // A tile's workgroups own row ranges; a row of block scales spans many
+  // tiles, so in the row-major layout one cache line of scales is written by
+  // the workgroups of many tiles. Where a tile's k-th row range always lands
+  // on die k (whole segments, a multiple of kXcds per tile, workgroups
+  // dispatched to the dies in turn) those writes meet in one L2. Otherwise,
+  // for one-byte scales (E8M0, E4M3) large enough to matter, the passes use
+  // a tile-major copy in the workspace: NVFP4 on 4096x14336 fetched and
+  // wrote 1.47x its algorithmic bytes with the row-major scales. fp16 scales
+  // stay row-major: in the Llama-3.1-8B set the copies of its 4096x14336
+  // matrices cost more than they saved (87.1 against 86.5 ms per step).
+  const int scale_bytes = p->a_fmt == DQ_SCALE_FP16 ? 2 : 1;
+  const bool aligned = g.S % g.L == 0 && (g.S / g.L) % dq::kXcds == 0;
+  w.a_tiled = !aligned && scale_bytes == 1 && p->rows * (p->cols / p->group) >= (int64_t(1) << 20);
+  w.a_work_bytes = w.a_tiled ? align256(dq::tile_major_a_bytes(g, p->group, scale_bytes)) : 0;
+  w.bytes = align256(std::max({align256(pass_bytes) + w.a_work_bytes, init_bytes, report_bytes}));
+  // with statistics: the partials, the (unused) room of the tile-major
+  // scales, the codes of a state, then the per-workgroup sums of a pass or
+  // of the final report
   const int code_bits = (p->grid == DQ_GRID_INT8 || p->grid == DQ_GRID_E4M3) ? 8 : 4;
   w.pass_bytes = align256(pass_bytes);
   w.codes_bytes = align256(size_t(p->rows) * size_t(p->cols) * code_bits / 8);
   const size_t sums_bytes = align256(size_t(std::max(g.n_wg, report_wg)) * 3 * sizeof(double));
-  w.stats_bytes = std::max(w.bytes, w.pass_bytes + w.codes_bytes + sums_bytes);
+  w.stats_bytes = std::max(w.bytes, w.pass_bytes + w.a_work_bytes + w.codes_bytes + sums_bytes);
   return w;
 }
 
@@ -216,15 +233,16 @@ int dq_bcd_iterate(const dq_problem* p, const void* W, void* a, uint16_t* b, int
     return DQ_ERR_WORKSPACE;
   double* part = static_cast<double*>(workspace);
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  const dq::IterStats its{stats, base + ws.pass_bytes,
-                          reinterpret_cast<double*>(base + ws.pass_bytes + ws.codes_bytes)};
+  uint8_t* codes = base + ws.pass_bytes + ws.a_work_bytes;
+  const dq::IterStats its{stats, codes, reinterpret_cast<double*>(codes + ws.codes_bytes)};
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
     if (n_iters == 0)  // row 0 alone: the state passed in, no code changed
       return hip_status(dq::launch_report<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, nullptr,
                                                          nullptr, stats, its.part, st));
-    return hip_status(
-        dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr, false, st));
+    void* a_work = ws.a_tiled && !stats ? base + ws.pass_bytes : nullptr;
+    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, stats ? &its : nullptr,
+                                                        false, a_work, st));
   });
 }
 
@@ -241,7 +259,8 @@ int dq_bcd_iterate_noalloc(const dq_problem* p, const void* W, void* a, uint16_t
   if (!part) return DQ_ERR_HIP;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
-    return hip_status(dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, false, st));
+    return hip_status(
+        dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, false, nullptr, st));
   });
 }
 
@@ -256,13 +275,14 @@ int dq_solve(const dq_problem* p, const void* W, void* a, uint16_t* b, int32_t n
   if (!workspace || workspace_bytes < ws.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return DQ_ERR_WORKSPACE;
   double* part = static_cast<double*>(workspace);
+  void* a_work = ws.a_tiled ? static_cast<uint8_t*>(workspace) + ws.pass_bytes : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return dispatch(*p, [&]<int WT, int GR, int AF, int G>() {
     hipError_t e = hipSuccess;
     if (n_iters == 0)
       e = dq::launch_init<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, st);
     else
-      e = dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, true, st);
+      e = dq::launch_iterate<WT, GR, AF, G>(W, a, b, part, ws.g, n_iters, nullptr, true, a_work, st);
     if (e == hipSuccess)
       e = dq::launch_pack<WT, GR, AF, G>(W, p->ldw, p->rows, p->cols, a, b, packed, st);
     return hip_status(e);

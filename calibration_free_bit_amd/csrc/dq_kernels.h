@@ -10,6 +10,7 @@ namespace dq {
 constexpr int kTileCols = 64;   // columns of one independent tile
 constexpr int kRowsPerStep = 64;  // rows of one BCD pass workgroup step
 constexpr int kPassGrid = 512;  // target workgroups of one BCD pass (two per CU)
+constexpr int kXcds = 8;        // dies; workgroups are dispatched to them in turn
 
 // Geometry of one BCD pass. Work is the flattened list of (tile, row step)
 // pairs, tile-major; workgroup w owns steps [w L, (w+1) L). The workgroups
@@ -25,7 +26,8 @@ struct PassGeom {
   int64_t max_seg;  // most segments any tile has
 };
 // Workspace: two alternating [n_tiles][max_seg][64][2] float64 buffers of
-// column partial sums.
+// column partial sums, then (for some shapes) the passes' tile-major copy of
+// the block scales.
 
 // Rows per chunk of the column-norm initialization's partial sums: 256, or
 // more when the chunk count would exceed the grid's y limit (65535). Its
@@ -69,10 +71,19 @@ struct IterStats {
 
 // n_iters BCD passes and the final column update; with from_init (and no
 // stats) the first pass starts from the absmax initialization it forms
-// itself, so a and b need not hold a state on entry.
+// itself, so a and b need not hold a state on entry. With a_work (no
+// stats), the passes keep the block scales there in the tile-major layout
+// [n_tiles][M][64 / G], copied from a first (unless from_init) and back to
+// a at the end; a_work holds tile_major_a_bytes.
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, const IterStats* stats, bool from_init, hipStream_t st);
+                          int n_iters, const IterStats* stats, bool from_init, void* a_work,
+                          hipStream_t st);
+
+// Bytes of the tile-major copy of the block scales (elements of 1 or 2 bytes).
+inline int64_t tile_major_a_bytes(const PassGeom& g, int group, int scale_bytes) {
+  return g.n_tiles * g.M * (kTileCols / group) * scale_bytes;
+}
 
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_pack(const void* W, int64_t ldw, int64_t M, int64_t N, const void* a,

@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
     bcd_pass_kernel(const void* __restrict__ W, const double* __restrict__ part_in, void* __restrict__ a_,
                     int32_t gM, int32_t gN, int32_t gldw, int32_t gS, int32_t gL, int32_t gtotal,
                     int32_t gn_tiles, int32_t gmax_seg, const uint16_t* __restrict__ b,
-                    double* __restrict__ part_out, PassStats st) {
+                    double* __restrict__ part_out, PassStats st, int32_t a_tiled) {
   // the geometry comes as 32-bit scalars so that it arrives in preloaded
   // kernel-argument registers
   PassGeom g;
@@ -450,6 +450,12 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
   const int sub = lane % LPR, rl = lane / LPR;
   const int64_t nblk = g.N / G;
   AT* __restrict__ a = reinterpret_cast<AT*>(a_);
+  // block scale of (row, column c of tile t): row-major [M][N / G] at
+  // row * N / G + c / G, or tile-major [n_tiles][M][64 / G] (one-byte
+  // scales only) at t * M * 64 / G + row * 64 / G + (c - 64 t) / G
+  constexpr int TB = kTileCols / G;
+  const bool tiled = AFMT != kScaleFp16 && a_tiled;
+  const int64_t a_rs = tiled ? TB : nblk;
   double st_sse = 0.0, st_w2 = 0.0;
   int st_changed = 0;
 
@@ -466,7 +472,8 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
     const int64_t tcol = (int64_t)tile * kTileCols;
     const int64_t col0 = tcol + sub * LC;
     const bool lane_cols_ok = col0 < g.N;
-    const int64_t ccol = lane_cols_ok ? col0 : 0;  // clamped column for loads
+    const int64_t ccol = lane_cols_ok ? col0 : (tiled ? tcol : 0);  // clamped column for loads
+    const int64_t a_tile = tiled ? ((int64_t)tile * g.M * TB + (ccol - tcol) / G) : ccol / G;
 
     // Raw loads of row steps, issued kPrefetch steps ahead of their use
     // (a ring of register buffers). Rows past M (last step of a tile) read
@@ -478,7 +485,7 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
       raw[slot].load(W, r * g.ldw + ccol);
       if constexpr (!INIT) {
 #pragma unroll
-        for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[r * nblk + (ccol + bl * BL) / G];
+        for (int bl = 0; bl < NB; ++bl) a_raw[slot][bl] = a[a_tile + r * a_rs + bl * BL / G];
       }
     };
     uint32_t step = f - tile * S32;
@@ -523,10 +530,10 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
     // W pointer (bytes) and block-scale index of this lane's row, advanced
     // by one step of RPS rows at a time.
     const int64_t wstep = (int64_t)RPS * g.ldw * EB;
-    const int64_t astep = (int64_t)RPS * nblk;
+    const int64_t astep = (int64_t)RPS * a_rs;
     uint32_t row = step * RPS + wave * RPW + rl;
     const char* wp = reinterpret_cast<const char*>(W) + ((int64_t)row * g.ldw + ccol) * EB;
-    int64_t ai = (int64_t)row * nblk + ccol / G;
+    int64_t ai = a_tile + (int64_t)row * a_rs;
 
     // One row step; the ring slot is a compile-time constant so that no
     // in-flight register is ever copied (the loop below is unrolled by
@@ -1097,41 +1104,138 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
 }
 
 template <int WT, int GRID, int AFMT, int G, int MODE>
-hipError_t launch_pass(const void* W, const double* in, void* a, uint16_t* b, double* out,
+hipError_t launch_pass(const void* W, const double* in, void* a, bool a_tiled, uint16_t* b, double* out,
                        const PassGeom& g, const PassStats& ps, hipStream_t st) {
   constexpr int LC = pass_lane_cols<AFMT>();
   bcd_pass_kernel<WT, GRID, AFMT, G, MODE, LC><<<(unsigned)g.n_wg, pass_threads<LC>(), 0, st>>>(
       W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
-      (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps);
+      (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps, a_tiled ? 1 : 0);
   return hipGetLastError();
 }
 
-// n_iters passes from the state (a, b) -- or, with from_init, from the
-// absmax initialization, which the first pass forms itself -- then the
-// final column update into b.
+// Block scales between the caller's row-major layout [M][N / G] and the
+// tile-major one [n_tiles][M][64 / G] of a call's passes. The 64 / G scales
+// of one (row, tile) form a unit. A workgroup moves 64 rows x 32 tiles
+// through LDS: eight unit loads per thread in flight, rows read across
+// tiles and tiles written down rows, both contiguous.
+constexpr int kRelayRows = 64, kRelayTiles = 32;
+template <int BYTES> struct UnitOf;
+template <> struct UnitOf<1> { using T = uint8_t; };
+template <> struct UnitOf<2> { using T = uint16_t; };
+template <> struct UnitOf<4> { using T = uint32_t; };
+template <> struct UnitOf<8> { using T = uint64_t; };
+
+template <int AFMT, int G, bool TO_TILED>
+__global__ void __launch_bounds__(256)
+    relayout_a_kernel(const void* __restrict__ src_, void* __restrict__ dst_, int64_t M, int64_t N) {
+  constexpr int TB = kTileCols / G;
+  using U = typename UnitOf<TB * sizeof(typename ScaleStore<AFMT>::T)>::T;
+  constexpr int kPer = kRelayRows * kRelayTiles / 256;  // units per thread
+  __shared__ U s[kRelayRows * (kRelayTiles + 1)];        // [row][tile], padded
+  const U* __restrict__ src = reinterpret_cast<const U*>(src_);
+  U* __restrict__ dst = reinterpret_cast<U*>(dst_);
+  const int64_t n_tiles = N / kTileCols;                  // N % 64 == 0 here
+  const int64_t n_tc = (n_tiles + kRelayTiles - 1) / kRelayTiles;
+  const int64_t r0 = (int64_t)(blockIdx.x / n_tc) * kRelayRows;
+  const int64_t t0 = (int64_t)(blockIdx.x % n_tc) * kRelayTiles;
+  U v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int r = TO_TILED ? i / kRelayTiles : i % kRelayRows;
+    const int t = TO_TILED ? i % kRelayTiles : i / kRelayRows;
+    const int64_t row = r0 + r, tile = t0 + t;
+    v[j] = 0;
+    if (row < M && tile < n_tiles) v[j] = TO_TILED ? src[row * n_tiles + tile] : src[tile * M + row];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int r = TO_TILED ? i / kRelayTiles : i % kRelayRows;
+    const int t = TO_TILED ? i % kRelayTiles : i / kRelayRows;
+    s[r * (kRelayTiles + 1) + t] = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    const int r = TO_TILED ? i % kRelayRows : i / kRelayTiles;
+    const int t = TO_TILED ? i / kRelayRows : i % kRelayTiles;
+    const int64_t row = r0 + r, tile = t0 + t;
+    if (row < M && tile < n_tiles) {
+      const U u = s[r * (kRelayTiles + 1) + t];
+      if (TO_TILED)
+        dst[tile * M + row] = u;
+      else
+        dst[row * n_tiles + tile] = u;
+    }
+  }
+}
+
+// The same, one scale at a time: for a last tile narrower than 64 columns,
+// or row-major scales not aligned to a unit.
+template <int AFMT, int G, bool TO_TILED>
+__global__ void __launch_bounds__(256)
+    relayout_a_scalar_kernel(const void* __restrict__ src_, void* __restrict__ dst_, int64_t M, int64_t N) {
+  using AT = typename ScaleStore<AFMT>::T;
+  constexpr int TB = kTileCols / G;
+  const AT* __restrict__ src = reinterpret_cast<const AT*>(src_);
+  AT* __restrict__ dst = reinterpret_cast<AT*>(dst_);
+  const int64_t nblk = N / G;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * nblk) return;
+  // consecutive threads: consecutive scales of a row
+  const int64_t row = idx / nblk, blk = idx - row * nblk, tile = blk / TB;
+  const int64_t tm = (tile * M + row) * TB + blk % TB;
+  if (TO_TILED)
+    dst[tm] = src[idx];
+  else
+    dst[idx] = src[tm];
+}
+
+template <int AFMT, int G, bool TO_TILED>
+hipError_t launch_relayout_a(const void* src, void* dst, const PassGeom& g, hipStream_t st) {
+  constexpr int U = kTileCols / G * sizeof(typename ScaleStore<AFMT>::T);
+  const uintptr_t row_major = reinterpret_cast<uintptr_t>(TO_TILED ? src : dst);
+  if (g.N % kTileCols == 0 && row_major % U == 0) {
+    const int64_t blocks =
+        ((g.M + kRelayRows - 1) / kRelayRows) * ((g.n_tiles + kRelayTiles - 1) / kRelayTiles);
+    relayout_a_kernel<AFMT, G, TO_TILED><<<(unsigned)blocks, 256, 0, st>>>(src, dst, g.M, g.N);
+  } else {
+    const int64_t n = g.M * (g.N / G);
+    relayout_a_scalar_kernel<AFMT, G, TO_TILED><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, dst, g.M, g.N);
+  }
+  return hipGetLastError();
+}
+
 template <int WT, int GRID, int AFMT, int G>
 hipError_t launch_iterate(const void* W, void* a, uint16_t* b, double* part, const PassGeom& g,
-                          int n_iters, const IterStats* stats, bool from_init, hipStream_t st) {
+                          int n_iters, const IterStats* stats, bool from_init, void* a_work,
+                          hipStream_t st) {
   // partial buffers alternate between passes: pass k reads the partials of
   // pass k-1 (its column update) and writes its own to the other buffer
   const int64_t half = g.n_tiles * g.max_seg * kTileCols * 2;
   hipError_t err = hipSuccess;
+  const bool tiled = a_work && !stats && n_iters > 0;
+  void* pa = tiled ? a_work : a;  // the block scales the passes read and write
+  if (tiled && !from_init) err = launch_relayout_a<AFMT, G, true>(a, a_work, g, st);
   for (int it = 0; it < n_iters && err == hipSuccess; ++it) {
     const double* in = it == 0 ? nullptr : part + ((it - 1) & 1) * half;
     double* out = part + (it & 1) * half;
     if (stats) {
       const PassStats ps{stats->codes, stats->part, it > 0 ? 1 : 0};
-      err = launch_pass<WT, GRID, AFMT, G, kPassStats>(W, in, a, b, out, g, ps, st);
+      err = launch_pass<WT, GRID, AFMT, G, kPassStats>(W, in, a, false, b, out, g, ps, st);
       if (err == hipSuccess) {
         report_reduce_kernel<<<1, 256, 0, st>>>(stats->part, g.n_wg, stats->out + 3 * it);
         err = hipGetLastError();
       }
     } else if (it == 0 && from_init) {
-      err = launch_pass<WT, GRID, AFMT, G, kPassInit>(W, in, a, b, out, g, PassStats{}, st);
+      err = launch_pass<WT, GRID, AFMT, G, kPassInit>(W, in, pa, tiled, b, out, g, PassStats{}, st);
     } else {
-      err = launch_pass<WT, GRID, AFMT, G, kPassPlain>(W, in, a, b, out, g, PassStats{}, st);
+      err = launch_pass<WT, GRID, AFMT, G, kPassPlain>(W, in, pa, tiled, b, out, g, PassStats{}, st);
     }
   }
+  if (err == hipSuccess && tiled) err = launch_relayout_a<AFMT, G, false>(a_work, a, g, st);
   if (err == hipSuccess && n_iters > 0) {
     bcd_column_kernel<<<(unsigned)g.n_tiles, kTileCols, 0, st>>>(part + ((n_iters - 1) & 1) * half, b, g);
     err = hipGetLastError();
@@ -1184,7 +1288,7 @@ hipError_t launch_act(const uint16_t* X, int64_t ldx, int64_t T, int64_t N, cons
                                                          void*, uint16_t*, double*, hipStream_t); \
   template hipError_t launch_iterate<WT, GR, AF, G>(const void*, void*, uint16_t*, double*,      \
                                                     const PassGeom&, int, const IterStats*, bool,  \
-                                                    hipStream_t);                                  \
+                                                    void*, hipStream_t);                           \
   template hipError_t launch_pack<WT, GR, AF, G>(const void*, int64_t, int64_t, int64_t,          \
                                                  const void*, const uint16_t*, uint8_t*,          \
                                                  hipStream_t);                                    \

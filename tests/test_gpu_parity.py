@@ -698,6 +698,44 @@ def test_full_size_sampled_stripes(wl_name, seed):
     np.testing.assert_array_equal(F.project(b, "fp16"), b)
 
 
+@pytest.mark.parametrize("name,M,N", [("nvfp4_g16", 2048, 8208), ("mxfp8_g32", 4096, 8224),
+                                       ("nvfp4_g16", 2100, 8256), ("mxfp8_g32", 4100, 8256)])
+def test_tile_major_scales(name, M, N):
+    """Shapes whose passes keep the block scales in the tile-major copy (the
+    segments of a tile do not fall on one die each, and the one-byte scales
+    pass 1 MiB): a last tile of 16 or 32 columns (the copy is made one scale
+    at a time), or whole tiles with a partial last band of 64 rows and of 32
+    tiles (one row's scales of a tile at a time). dq_solve (the first pass
+    writes the copy), init + dq_bcd_iterate (the copy is filled from a) and
+    init + dq_bcd_iterate_noalloc (row-major scales throughout) must agree
+    bit for bit, and whole stripes, the ragged one included, match the
+    oracle."""
+    fmt = dq.FORMATS[name]
+    ofmt = oracle_fmt(fmt)
+    T = 3
+    data = _mat(M, N, 31)
+    print(f"[case] tile-major scales {name} {M}x{N} T={T}", flush=True)
+    g = DeviceRun(data, fmt).solve(T)
+    sep = DeviceRun(data, fmt).run(T)
+    assert torch.equal(g.s.a, sep.s.a) and torch.equal(g.s.b, sep.s.b)
+    assert torch.equal(g.s.packed, sep.s.packed)
+    na = DeviceRun(data, fmt)
+    na.s.init()
+    dq.bcd_iterate_noalloc(na.s.p, na.W, na.s.a, na.s.b, T)
+    torch.cuda.synchronize()
+    assert torch.equal(g.s.a, na.s.a) and torch.equal(g.s.b, na.s.b)
+    del sep, na
+    a, b, Q = g.a, g.b, g.Q
+    G = fmt.group
+    n_str = N // G
+    W64 = as_f64(data)
+    for s in (0, 1, n_str // 2, n_str - 2, n_str - 1):
+        cs = slice(s * G, s * G + G)
+        sol = D.solve(W64[:, cs], ofmt, T)
+        r = compare(W64[:, cs], a[:, s:s + 1], b[cs], Q[:, cs], sol, ofmt, f"{name} stripe {s}")
+        assert r == {"a_diff": 0, "b_diff": 0, "q_diff": 0}, (s, r)
+
+
 @pytest.mark.parametrize("aw_name", sorted(synth.ACT_WORKLOADS))
 def test_activation_full_size_sampled_tokens(aw_name):
     """The benchmarked activation batches at full size, in the launch the
