@@ -706,10 +706,10 @@ def test_tile_major_scales(name, M, N):
     pass 1 MiB): a last tile of 16 or 32 columns (the copy is made one scale
     at a time), or whole tiles with a partial last band of 64 rows and of 32
     tiles (one row's scales of a tile at a time). dq_solve (the first pass
-    writes the copy), init + dq_bcd_iterate (the copy is filled from a) and
-    init + dq_bcd_iterate_noalloc (row-major scales throughout) must agree
-    bit for bit, and whole stripes, the ragged one included, match the
-    oracle."""
+    writes the copy), init + dq_bcd_iterate (the copy is filled from a, also
+    from an a at an odd address) and init + dq_bcd_iterate_noalloc
+    (row-major scales throughout) must agree bit for bit, and whole stripes,
+    the ragged one included, match the oracle."""
     fmt = dq.FORMATS[name]
     ofmt = oracle_fmt(fmt)
     T = 3
@@ -724,7 +724,16 @@ def test_tile_major_scales(name, M, N):
     dq.bcd_iterate_noalloc(na.s.p, na.W, na.s.a, na.s.b, T)
     torch.cuda.synchronize()
     assert torch.equal(g.s.a, na.s.a) and torch.equal(g.s.b, na.s.b)
-    del sep, na
+    # block scales at an odd address: the copy is made one scale at a time
+    mis = DeviceRun(data, fmt)
+    mis.s.init()
+    buf = torch.empty(mis.s.a.numel() + 1, dtype=torch.uint8, device="cuda")
+    a_odd = buf[1:].view(mis.s.a.shape)
+    a_odd.copy_(mis.s.a)
+    dq.bcd_iterate(mis.s.p, mis.W, a_odd, mis.s.b, T, mis.s.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(g.s.a, a_odd) and torch.equal(g.s.b, mis.s.b)
+    del sep, na, mis
     a, b, Q = g.a, g.b, g.Q
     G = fmt.group
     n_str = N // G
