@@ -223,9 +223,6 @@ template <> struct Grid<kGridInt4> {
     const float up = (d > 0.0f || (d == 0.0f && k_odd)) ? 1.0f : 0.0f;
     return __builtin_amdgcn_fmed3f(k + up, -8.0f, 7.0f);
   }
-  __device__ static __forceinline__ uint32_t nibble(float q) {
-    return (uint32_t)((int)q) & 0xFu;
-  }
   // Codes of N estimates; true if any of them may round differently at the
   // exact quotient (then the caller re-decides those with exact(); near()
   // tells which). diff is unused here.
@@ -249,12 +246,16 @@ template <> struct Grid<kGridInt4> {
 #pragma unroll
     for (int e = 0; e < N; ++e) q[e] = __builtin_rintf(__builtin_amdgcn_fmed3f(y[e], -8.25f, 7.25f));
   }
-  // Nibbles of 8 codes, element k in bits 4k..4k+3.
+  // Nibbles of 8 codes, element k in bits 4k..4k+3 (two's complement). A
+  // pair of codes offset by 8 is the byte 16 (q1 + 8) + (q0 + 8), an exact
+  // integer in [0, 255] that the byte conversion packs in place; flipping
+  // bit 3 of each offset nibble gives the two's complement nibble.
   __device__ static __forceinline__ uint32_t pack8(const float* q) {
     uint32_t w = 0u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w |= nibble(q[k]) << (4 * k);
-    return w;
+    for (int p = 0; p < 4; ++p)
+      w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[2 * p + 1], 16.0f, q[2 * p] + 136.0f), p, w);
+    return w ^ 0x88888888u;
   }
   // 8 codes in storage form, and the number of codes two such words differ in.
   using Word = uint32_t;
@@ -478,11 +479,14 @@ template <> struct Grid<kGridInt8> {
   }
   // 8 codes as two's complement bytes (8 bytes, 8-byte aligned when stored).
   using Word = uint2;
+  // Bytes of 8 codes (two's complement): each code offset by 128, an exact
+  // integer in [1, 255], packed in place by the byte conversion, then the
+  // offset's top bit flipped.
   __device__ static __forceinline__ Word encode8(const float* q) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k >> 2] |= ((uint32_t)((int)q[k]) & 0xFFu) << (8 * (k & 3));
-    return make_uint2(w[0], w[1]);
+    for (int k = 0; k < 8; ++k) w[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(q[k] + 128.0f, k & 3, w[k >> 2]);
+    return make_uint2(w[0] ^ 0x80808080u, w[1] ^ 0x80808080u);
   }
   __device__ static __forceinline__ int count_diff(Word x, Word y) {
     return bytes_differ(x.x ^ y.x) + bytes_differ(x.y ^ y.y);

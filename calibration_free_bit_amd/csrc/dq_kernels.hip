@@ -117,6 +117,21 @@ __device__ __forceinline__ double half_mirror(double v) {
   const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), 0x141, 0xF, 0xF, false);
   return __hiloint2double(hi, lo);
 }
+// Largest v over the aligned group of K lanes (K = 1, 2, 4 or 8) holding
+// this lane, for v >= 0 and not NaN (a block's absolute maximum, where the
+// per-lane maxima already dropped NaN). Such floats order as their bit
+// patterns, so each step is one unsigned max with the DPP move folded in
+// (a float max would first quiet the moved value).
+template <int K>
+__device__ __forceinline__ float max_join(float v) {
+  static_assert(K == 1 || K == 2 || K == 4 || K == 8, "groups of 1, 2, 4 or 8 lanes");
+  uint32_t u = __float_as_uint(v);
+  if constexpr (K >= 2) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  if constexpr (K >= 4) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  if constexpr (K >= 8) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  return __uint_as_float(u);
+}
+
 // Sum of v over the aligned group of K lanes (K = 1, 2, 4 or 8) holding
 // this lane, in every lane of the group: pairs, then quads, then the two
 // quads of a group of 8. The order of the additions is fixed.
@@ -267,18 +282,8 @@ __global__ void __launch_bounds__(256) colnorm_a_kernel(const void* __restrict__
       wmax = __builtin_fmaxf(wmax, aw);
       ymax = __builtin_fmaxf(ymax, aw * rb[k]);
     }
-    if constexpr (LPB >= 2) {
-      wmax = __builtin_fmaxf(wmax, quad_xor<1>(wmax));
-      ymax = __builtin_fmaxf(ymax, quad_xor<1>(ymax));
-    }
-    if constexpr (LPB >= 4) {
-      wmax = __builtin_fmaxf(wmax, quad_xor<2>(wmax));
-      ymax = __builtin_fmaxf(ymax, quad_xor<2>(ymax));
-    }
-    if constexpr (LPB >= 8) {
-      wmax = __builtin_fmaxf(wmax, half_mirror(wmax));
-      ymax = __builtin_fmaxf(ymax, half_mirror(ymax));
-    }
+    wmax = max_join<LPB>(wmax);
+    ymax = max_join<LPB>(ymax);
     // a zero block is exactly the case wmax == 0; a non-zero block whose
     // float32 quotients underflow is left to the certified path's range test
     bool unsure = false;
@@ -574,9 +579,7 @@ __global__ void __launch_bounds__(pass_threads<LC>(), pass_threads<LC>() / 128)
 #pragma unroll
           for (int k = 0; k < BL; ++k) amax[bl] = __builtin_fmaxf(amax[bl], __builtin_fabsf(w[bl * BL + k]));
         }
-        if constexpr (LPB >= 2) amax[0] = __builtin_fmaxf(amax[0], quad_xor<1>(amax[0]));
-        if constexpr (LPB >= 4) amax[0] = __builtin_fmaxf(amax[0], quad_xor<2>(amax[0]));
-        if constexpr (LPB >= 8) amax[0] = __builtin_fmaxf(amax[0], half_mirror(amax[0]));
+        amax[0] = max_join<LPB>(amax[0]);
         bool unsure = false;
 #pragma unroll
         for (int bl = 0; bl < NB; ++bl)
@@ -1033,9 +1036,7 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
       amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
     }
     static_assert(LPB <= 8, "a block's lanes lie in one group of 8");
-    if constexpr (LPB >= 2) amax = __builtin_fmaxf(amax, quad_xor<1>(amax));
-    if constexpr (LPB >= 4) amax = __builtin_fmaxf(amax, quad_xor<2>(amax));
-    if constexpr (LPB >= 8) amax = __builtin_fmaxf(amax, half_mirror(amax));
+    amax = max_join<LPB>(amax);
     bool unsure = false;
     float sf = ls_scale_fast<AFMT>((double)amax, (double)Grid<GRID>::qmax, unsure);
     if (wave_any(unsure))

@@ -699,18 +699,20 @@ def test_full_size_sampled_stripes(wl_name, seed):
 
 
 @pytest.mark.parametrize("name,M,N", [("nvfp4_g16", 2048, 8208), ("mxfp8_g32", 4096, 8224),
-                                       ("nvfp4_g16", 2100, 8256), ("mxfp8_g32", 4100, 8256)])
+                                       ("nvfp4_g16", 2100, 8256), ("mxfp8_g32", 4100, 8256),
+                                       ("e2m1_g64_e4m3", 8200, 8256)])
 def test_tile_major_scales(name, M, N):
     """Shapes whose passes keep the block scales in the tile-major copy (the
     segments of a tile do not fall on one die each, and the one-byte scales
     pass 1 MiB): a last tile of 16 or 32 columns (the copy is made one scale
     at a time), or whole tiles with a partial last band of 64 rows and of 32
-    tiles (one row's scales of a tile at a time). dq_solve (the first pass
+    tiles (one row's scales of a tile at a time: 4, 2 or 1 bytes for groups of
+    16, 32 or 64). dq_solve (the first pass
     writes the copy), init + dq_bcd_iterate (the copy is filled from a, also
     from an a at an odd address) and init + dq_bcd_iterate_noalloc
     (row-major scales throughout) must agree bit for bit, and whole stripes,
     the ragged one included, match the oracle."""
-    fmt = dq.FORMATS[name]
+    fmt = dq.FORMATS[name] if name in dq.FORMATS else ALL_FORMATS[name]
     ofmt = oracle_fmt(fmt)
     T = 3
     data = _mat(M, N, 31)
