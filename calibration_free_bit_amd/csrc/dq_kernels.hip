@@ -1107,7 +1107,11 @@ hipError_t launch_init_colnorm(const void* W, int64_t ldw, int64_t M, int64_t N,
 template <int WT, int GRID, int AFMT, int G, int MODE>
 hipError_t launch_pass(const void* W, const double* in, void* a, bool a_tiled, uint16_t* b, double* out,
                        const PassGeom& g, const PassStats& ps, hipStream_t st) {
-  constexpr int LC = pass_lane_cols<AFMT>();
+  // The first pass of a solve reads W cold from HBM: it takes the 8-column
+  // form for every format, whose four waves per SIMD keep more loads in
+  // flight (solves from the absmax start with W evicted: 14336x4096 INT4-G64
+  // 777 -> 773 us, 4096x14336 831 -> 821 us).
+  constexpr int LC = MODE == kPassInit ? 8 : pass_lane_cols<AFMT>();
   bcd_pass_kernel<WT, GRID, AFMT, G, MODE, LC><<<(unsigned)g.n_wg, pass_threads<LC>(), 0, st>>>(
       W, in, a, (int32_t)g.M, (int32_t)g.N, (int32_t)g.ldw, (int32_t)g.S, (int32_t)g.L,
       (int32_t)g.total, (int32_t)g.n_tiles, (int32_t)g.max_seg, b, out, ps, a_tiled ? 1 : 0);
